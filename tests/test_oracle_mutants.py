@@ -1,0 +1,94 @@
+"""The oracle's pins must catch plausible mistakes.
+
+Each case plants one slip in a copy of the oracle's C source (on the CPU, in a
+temporary directory), builds it with gcc, and checks that the independent
+torch-SDPA construction then disagrees with it.  The unmodified source must
+agree.  This guards the pins themselves: a pin that a dropped scale, a wrong
+causal bound or a wrong head group cannot fail would be worthless.
+"""
+import os
+import subprocess
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from speculative_decoding_attention_amd import workloads as W
+from test_oracle_pins import sdpa_reference
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "verify_attn_oracle.c")
+
+MUTANTS = {
+    "k_scale dropped from prefix score": [
+        ("sc[j] = sm_scale * k_scale * dot;", "sc[j] = sm_scale * dot;")],
+    "k_scale applied to draft score": [
+        ("sc[n_pre + j] = sm_scale * dot;", "sc[n_pre + j] = sm_scale * k_scale * dot;")],
+    "v_scale dropped from prefix value": [
+        ("acc[c] += w * v_scale * pool_elem", "acc[c] += w * pool_elem")],
+    "v_scale applied to draft value": [
+        ("acc[c] += w * oracle_bf16_to_f64(v_ext", "acc[c] += w * v_scale * oracle_bf16_to_f64(v_ext")],
+    "strict causal bound j < i": [
+        ("for (int j = 0; j <= i; ++j)", "for (int j = 0; j < i; ++j)")],
+    "draft keys from the query row": [
+        ("k_ext[(row0 + j) * ke_s0", "k_ext[(row0 + i) * ke_s0")],
+    "heads grouped round-robin": [
+        ("const int g = h / group;", "const int g = h % h_kv;")],
+    "query cast applied to draft": [
+        ("dot += qv[c] * oracle_bf16_to_f64(k_ext", "dot += qh[c] * oracle_bf16_to_f64(k_ext")],
+    "query cast omitted": [
+        ("qh[c] = kv_is_fp8 ? oracle_e4m3fn_to_f64(oracle_f64_to_e4m3fn(qv[c])) : qv[c];",
+         "qh[c] = qv[c];")],
+    "e4m3 exponent bias 8": [
+        ("v = ldexp(1.0 + (double)m / 8.0, e - 7);", "v = ldexp(1.0 + (double)m / 8.0, e - 8);")],
+    "e4m3 cast truncates": [
+        ("double r = nearbyint(q);", "double r = floor(q);")],
+}
+
+
+def _problems():
+    bf = W.make_problem([33, 0, 21], 4, 8, 2, 32, 24, k_scale=0.5, v_scale=0.25,
+                        pool_factor=2, permute=True, seed=41)
+    f8 = W.make_problem([25, 7], 4, 4, 1, 32, 32, kv_dtype=torch.float8_e4m3fn,
+                        pool_factor=2, permute=True, seed=42)
+    f8.q.mul_(7.0)
+    return [bf, f8]
+
+
+def _max_err(lib, probs):
+    err = 0.0
+    for p in probs:
+        got = oracle.verify_attn(p.q, p.k_ext, p.v_ext, p.k_buf, p.v_buf, p.qo_indptr,
+                                 p.kv_indptr, p.kv_indices, p.sm_scale, p.k_scale,
+                                 p.v_scale, lib=lib)
+        err = max(err, float(np.abs(got - sdpa_reference(p)).max()))
+    return err
+
+
+def _build(src_text, tmp_path, name):
+    c = tmp_path / (name + ".c")
+    so = tmp_path / (name + ".so")
+    c.write_text(src_text)
+    subprocess.run(["gcc", "-O1", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-o", str(so),
+                    str(c), "-lm"], check=True)
+    return oracle.load_variant(str(so))
+
+
+@pytest.fixture(scope="module")
+def probs():
+    return _problems()
+
+
+def test_unmodified_source_agrees(tmp_path, probs):
+    lib = _build(open(SRC).read(), tmp_path, "orig")
+    assert _max_err(lib, probs) < 1e-12
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path, probs):
+    text = open(SRC).read()
+    for old, new in MUTANTS[name]:
+        assert old in text, "mutation anchor not found: %r" % old
+        text = text.replace(old, new)
+    lib = _build(text, tmp_path, "mut")
+    assert _max_err(lib, probs) > 1e-6, "pins did not catch: " + name
