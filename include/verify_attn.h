@@ -1,0 +1,193 @@
+/*
+ * verify_attn.h -- C ABI of the MI355X (gfx950) split-KV target-verify
+ * attention library (speculative decoding, topk = 1).
+ *
+ * The operation is the one sglang's "verify_splitkv.py" defines (module
+ * docstring; kernels _verify_prefix_stage1 and _verify_combine_stage2; entry
+ * verify_splitkv_fwd): each sequence b has a prefix of n_b tokens in a paged
+ * KV pool and l_ext draft tokens.  Draft query row i of query head h attends
+ *   - to every prefix token (no mask), score = sm_scale * k_scale *
+ *     <cast_to_pool_dtype(q), K_pool[row]>, value = v_scale * V_pool[row];
+ *   - to the draft tokens j <= i of its own sequence (causal), score =
+ *     sm_scale * <q, K_ext[j]>, value = V_ext[j] (no cast, no scale);
+ * with one softmax over both.  Query heads are grouped contiguously per KV
+ * head (kv_head = h / (h_q / h_kv)).
+ *
+ * Execution: two kernels on the caller's stream.  The prefix pass splits every
+ * sequence's prefix into ranges processed in parallel; each range writes a
+ * normalised partial output and its log-sum-exp into the caller's workspace.
+ * The combine pass merges the ranges by log-sum-exp, computes the small causal
+ * draft block and merges the two.  No call allocates, synchronises, or reads
+ * device memory on the host, so every call may be captured into a HIP graph.
+ *
+ * Pointers: every tensor pointer is a device pointer (HIP device memory of the
+ * current device).  The caller owns every buffer; the library keeps no
+ * reference after a call returns.  Element strides are in elements of the
+ * tensor's own type; the last dimension of every tensor must be contiguous.
+ *
+ * Errors: every entry point returns VA_OK (0) or a negative va_status_t and
+ * does nothing else on error.  verify_attn_last_error() gives a message for
+ * the most recent error on the calling thread.
+ */
+#ifndef VERIFY_ATTN_H
+#define VERIFY_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VA_API __attribute__((visibility("default")))
+
+/* Element type of the prefix pool (k_buf, v_buf).  q, k_ext, v_ext and out
+ * are always bf16.  FP8_E4M3FN is the OCP 8-bit format (bias 7, max 448). */
+typedef enum {
+    VA_DTYPE_BF16 = 0,
+    VA_DTYPE_FP8_E4M3FN = 1
+} va_dtype_t;
+
+typedef enum {
+    VA_OK = 0,
+    VA_ERR_NULL_ARG = -1,   /* a required pointer is NULL */
+    VA_ERR_BATCH = -2,      /* bs < 1 */
+    VA_ERR_HEADS = -3,      /* h_q or h_kv < 1, or h_q % h_kv != 0 */
+    VA_ERR_HEAD_DIM = -4,   /* head_dim != v_head_dim or not in {64,128,256} */
+    VA_ERR_DTYPE = -5,      /* kv_dtype not a va_dtype_t */
+    VA_ERR_EXTEND = -6,     /* l_ext < 1, or q_rows != bs * l_ext (ragged extend) */
+    VA_ERR_STRIDE = -7,     /* stride not positive, rows overlap, or row start not 16-B aligned */
+    VA_ERR_SCALE = -8,      /* sm_scale, k_scale or v_scale not finite or <= 0 */
+    VA_ERR_WORKSPACE = -9,  /* workspace NULL or smaller than the plan's size */
+    VA_ERR_SPLIT = -10,     /* split_tokens not a multiple of 64, or both split fields set */
+    VA_ERR_ALIGN = -11,     /* a tensor base pointer is not 16-byte aligned */
+    VA_ERR_DEVICE = -12,    /* a HIP runtime call failed (device query or launch) */
+    VA_ERR_SIZE = -13       /* a size is negative or exceeds the kernels' index range */
+} va_status_t;
+
+/* Static problem description: shapes, strides and the pool dtype.  Every
+ * field is a host value; nothing here is read from device memory.
+ *   q      [q_rows, h_q,  head_dim]    bf16     strides q_stride[0..1]
+ *   k_ext  [q_rows, h_kv, head_dim]    bf16     strides kext_stride[0..1]
+ *   v_ext  [q_rows, h_kv, v_head_dim]  bf16     strides vext_stride[0..1]
+ *   k_buf  [pool,   h_kv, head_dim]    kv_dtype strides kbuf_stride[0..1]
+ *   v_buf  [pool,   h_kv, v_head_dim]  kv_dtype strides vbuf_stride[0..1]
+ *   out    [q_rows, h_q,  v_head_dim]  bf16     strides out_stride[0..1]
+ * num_kv_indices is the length of kv_indices (a static shape; it bounds the
+ * work-item count, so it must be >= kv_indptr[bs] - kv_indptr[0]).
+ * Splitting (both 0 = the library's static heuristic):
+ *   split_tokens > 0 : every prefix is cut into ranges of split_tokens tokens
+ *                      (a multiple of 64); ranges are work items;
+ *   n_splits > 0     : the pages' rule -- every prefix is cut into n_splits
+ *                      ranges of ceil(ceil(n_b / n_splits) / 32) * 32 tokens;
+ *                      ranges past the end are empty.
+ * The result does not depend on the split beyond floating-point rounding. */
+typedef struct {
+    int32_t bs;
+    int32_t h_q;
+    int32_t h_kv;
+    int32_t head_dim;
+    int32_t v_head_dim;
+    int32_t kv_dtype;
+    int64_t q_rows;
+    int64_t num_kv_indices;
+    int64_t q_stride[2];
+    int64_t kext_stride[2];
+    int64_t vext_stride[2];
+    int64_t kbuf_stride[2];
+    int64_t vbuf_stride[2];
+    int64_t out_stride[2];
+    int32_t split_tokens;
+    int32_t n_splits;
+} va_desc_t;
+
+/* Launch plan derived from a descriptor (pure function of the descriptor,
+ * l_ext and the CU count; identical for every call with the same inputs, so a
+ * workspace sized once stays valid, as graph capture needs). */
+typedef struct {
+    int32_t mode;            /* 0: fixed-size ranges; 1: n_splits equal ranges per sequence */
+    int32_t split_tokens;    /* tokens per range (mode 0) */
+    int32_t n_splits;        /* ranges per sequence (mode 1) */
+    int32_t rows;            /* query rows per KV head: (h_q / h_kv) * l_ext */
+    int32_t row_chunks;      /* rows are processed in chunks of at most 64 */
+    int32_t tile_tokens;     /* prefix tokens per LDS tile in the prefix kernel */
+    int64_t range_slots;     /* upper bound on prefix ranges over the batch (per KV head) */
+    int64_t prefix_blocks;   /* grid of the prefix kernel (workgroups of 256 threads) */
+    int64_t combine_blocks;  /* grid of the combine kernel (workgroups of 256 threads) */
+    size_t workspace_bytes;  /* bytes of workspace the two passes need */
+    size_t partial_bytes;    /* of which: fp32 partial outputs */
+} va_plan_t;
+
+/* Validate a descriptor (host only; no HIP call).
+ * Mirrors can_handle() in verify_splitkv.py, which accepts only causal topk=1
+ * verify with a constant extend length: bs >= 1, h_q % h_kv == 0, consistent
+ * head dims, q_rows == bs * l_ext.  Returns VA_OK or the first failing code. */
+VA_API int verify_attn_check(const va_desc_t *desc, int32_t l_ext);
+
+/* Compute the launch plan.  num_cus > 0 uses that CU count (pure host);
+ * num_cus <= 0 queries the current HIP device once and caches it per device.
+ * The static split heuristic needs only shapes (no device read), the
+ * capture-safety constraint stated in verify_splitkv.py's choose_n_splits. */
+VA_API int verify_attn_plan(const va_desc_t *desc, int32_t l_ext, int32_t num_cus,
+                            va_plan_t *plan);
+
+/* Workspace size in bytes for (desc, l_ext) on a device with num_cus CUs
+ * (num_cus <= 0: the current device).  Equals plan.workspace_bytes. */
+VA_API int verify_attn_workspace_bytes(const va_desc_t *desc, int32_t l_ext, int32_t num_cus,
+                                       size_t *bytes);
+
+/* Full verify attention: the prefix pass then the combine pass, both on
+ * `stream` (a hipStream_t; NULL = the default stream).
+ *   q, k_ext, v_ext   draft queries / keys / values (bf16, layouts above)
+ *   k_buf, v_buf      prefix pool (desc->kv_dtype)
+ *   qo_indptr [bs+1]  int32; must equal b * l_ext (constant extend length)
+ *   kv_indptr [bs+1]  int32; non-decreasing prefix offsets into kv_indices
+ *   kv_indices        int64 pool row of every prefix token, each in [0, pool)
+ *   sm_scale          softmax scale (1/sqrt(head_dim) is the usual value)
+ *   k_scale, v_scale  pool dequant multipliers on prefix scores / prefix values
+ *   out               bf16 output, written in full (rounded to nearest even)
+ *   workspace         device buffer of at least verify_attn_workspace_bytes()
+ * The qo_indptr / kv_indptr / kv_indices preconditions are not checked on the
+ * host (that would need a device read); violating them is undefined. */
+VA_API int verify_attn_run(const void *q, const void *k_ext, const void *v_ext,
+                           const void *k_buf, const void *v_buf,
+                           const int32_t *qo_indptr, const int32_t *kv_indptr,
+                           const int64_t *kv_indices, int32_t l_ext,
+                           float sm_scale, float k_scale, float v_scale, void *out,
+                           const va_desc_t *desc, void *workspace, size_t workspace_bytes,
+                           void *stream);
+
+/* Prefix pass only (the pages' _verify_prefix_stage1): writes, for every range
+ * and query row, the v_scale-multiplied normalised partial output (fp32) and
+ * its natural log-sum-exp into the workspace; an empty range writes output 0
+ * and log-sum-exp -inf.  Arguments as for verify_attn_run. */
+VA_API int verify_attn_prefix(const void *q, const void *k_buf, const void *v_buf,
+                              const int32_t *qo_indptr, const int32_t *kv_indptr,
+                              const int64_t *kv_indices, int32_t l_ext,
+                              float sm_scale, float k_scale, float v_scale,
+                              const va_desc_t *desc, void *workspace, size_t workspace_bytes,
+                              void *stream);
+
+/* Combine pass only (the pages' _verify_combine_stage2): log-sum-exp merge of
+ * the ranges written by verify_attn_prefix, the causal draft block, the final
+ * two-way merge and the bf16 store into out.  Arguments as for verify_attn_run. */
+VA_API int verify_attn_combine(const void *q, const void *k_ext, const void *v_ext,
+                               const int32_t *qo_indptr, const int32_t *kv_indptr,
+                               int32_t l_ext, float sm_scale, void *out,
+                               const va_desc_t *desc, void *workspace, size_t workspace_bytes,
+                               void *stream);
+
+/* Static text for a status code. */
+VA_API const char *verify_attn_strerror(int code);
+
+/* Message for the most recent error on the calling thread ("" if none). */
+VA_API const char *verify_attn_last_error(void);
+
+/* Library ABI version (major * 10000 + minor * 100 + patch). */
+VA_API int verify_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VERIFY_ATTN_H */

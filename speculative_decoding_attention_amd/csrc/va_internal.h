@@ -1,0 +1,81 @@
+// va_internal.h -- internal definitions shared by the host side and the HIP
+// kernels of the verify-attention library.  Not part of the public ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "verify_attn.h"
+
+namespace va {
+
+// Rows of one KV head's query tile are processed in chunks of at most this
+// many rows (4 MFMA row blocks of 16).
+constexpr int kRowChunk = 64;
+// Granule of the pages' equal-split rule (ranges are rounded up to it).
+constexpr int kEvenSplitGranule = 32;
+// Threads per workgroup of both kernels (4 wavefronts of 64).
+constexpr int kThreads = 256;
+// Prefix kernel workgroups resident per CU the split heuristic aims for.
+constexpr int kResidentPerCU = 2;
+// Smallest range the heuristic chooses; ranges are multiples of this.
+constexpr int kSplitQuantum = 64;
+
+// Prefix tokens per LDS tile: a D=256 tile of 32 tokens holds 32 KB of K+V in
+// bf16, a D<=128 tile 64 tokens (<= 32 KB).
+constexpr int tile_tokens_for(int head_dim) { return head_dim == 256 ? 32 : 64; }
+
+// 16-row MFMA blocks per row chunk (1, 2 or 4).
+inline int row_blocks_for(int rows_in_chunk)
+{
+    int mb = (rows_in_chunk + 15) / 16;
+    return mb <= 1 ? 1 : (mb <= 2 ? 2 : 4);
+}
+
+struct PrefixParams {
+    const uint16_t *q;
+    const uint8_t *k_buf;  // byte pointers: the pool is bf16 or fp8
+    const uint8_t *v_buf;
+    const int32_t *qo_indptr;
+    const int32_t *kv_indptr;
+    const int64_t *kv_indices;
+    float *part_o;    // [range_slots * h_kv, rows, D] fp32
+    float *part_lse;  // [range_slots * h_kv, rows]    fp32 (natural log)
+    int64_t q_s0, q_s1;        // elements
+    int64_t kb_s0, kb_s1;      // bytes
+    int64_t vb_s0, vb_s1;      // bytes
+    float qk_scale_log2;       // sm_scale * k_scale * log2(e)
+    float v_scale;
+    int32_t bs, h_kv, group, l_ext, rows, row_chunks;
+    int32_t mode, split_tokens, n_splits;
+};
+
+struct CombineParams {
+    const uint16_t *q;
+    const uint16_t *k_ext;
+    const uint16_t *v_ext;
+    const int32_t *qo_indptr;
+    const int32_t *kv_indptr;
+    const float *part_o;
+    const float *part_lse;
+    uint16_t *out;
+    int64_t q_s0, q_s1, ke_s0, ke_s1, ve_s0, ve_s1, o_s0, o_s1;  // elements
+    float sm_scale;
+    int32_t bs, h_kv, group, l_ext, rows;
+    int32_t mode, split_tokens, n_splits;
+};
+
+// Launchers (defined in va_kernels.hip).  Return a hipError_t value.
+int launch_prefix(const PrefixParams &p, int head_dim, bool kv_fp8, int row_blocks,
+                  int64_t blocks, void *stream);
+int launch_combine(const CombineParams &p, int head_dim, int64_t blocks, void *stream);
+const char *hip_error_string(int err);
+
+// Host-side validation and planning (defined in va_plan.cpp).
+int check_desc(const va_desc_t *d, int32_t l_ext);
+int make_plan(const va_desc_t *d, int32_t l_ext, int32_t num_cus, va_plan_t *plan);
+int current_device_cus(int32_t *cus);
+void set_error(const char *fmt, ...);
+void clear_error();
+
+}  // namespace va

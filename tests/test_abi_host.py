@@ -1,0 +1,143 @@
+"""Host-only tests of the C-ABI library: exports, validation, the static plan.
+
+No test here launches a kernel; they run without a GPU.  Validation mirrors
+can_handle() in sglang's verify_splitkv.py and its fallback tests in
+test_verify_splitkv.py (non-causal / exotic features have no parameter in this
+ABI; the ragged-extend case maps to q_rows != bs * l_ext).
+"""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+import torch
+
+from speculative_decoding_attention_amd import verify_attn as va
+from speculative_decoding_attention_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "verify_attn.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return re.findall(r"VA_API\s+[\w\s\*]+?\b(verify_attn_\w+)\s*\(", text)
+
+
+def test_header_declares_the_documented_entry_points():
+    names = set(declared_symbols())
+    assert {"verify_attn_run", "verify_attn_prefix", "verify_attn_combine", "verify_attn_check",
+            "verify_attn_plan", "verify_attn_workspace_bytes", "verify_attn_strerror",
+            "verify_attn_last_error", "verify_attn_version"} <= names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(va.LIB_PATH)
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+    assert va.lib().verify_attn_version() >= 100
+
+
+def meta_problem(bs=3, l_ext=4, h_q=16, h_kv=2, d=256, n=512, kv_dtype=torch.bfloat16, **kw):
+    m = lambda *s, dt=torch.bfloat16: torch.empty(*s, dtype=dt, device="meta")
+    q = m(bs * l_ext, h_q, d)
+    return dict(q=q, k_ext=m(bs * l_ext, h_kv, d), v_ext=m(bs * l_ext, h_kv, d),
+                k_buf=m(bs * n, h_kv, d, dt=kv_dtype), v_buf=m(bs * n, h_kv, d, dt=kv_dtype),
+                kv_indices=m(bs * n, dt=torch.int64), out=m(bs * l_ext, h_q, d), bs=bs, **kw)
+
+
+def desc_of(**kw):
+    return va.make_desc(**meta_problem(**kw))
+
+
+def test_valid_descriptor_passes():
+    assert va.verify_attn_check(desc_of(), 4) == 0
+    assert va.verify_attn_check(desc_of(kv_dtype=torch.float8_e4m3fn, d=128, h_q=8, h_kv=1), 4) == 0
+
+
+@pytest.mark.parametrize("mutate,l_ext,code", [
+    (lambda d: setattr(d, "bs", 0), 4, -2),
+    (lambda d: setattr(d, "h_kv", 3), 4, -3),          # 16 % 3 != 0
+    (lambda d: setattr(d, "h_kv", 0), 4, -3),
+    (lambda d: setattr(d, "head_dim", 96), 4, -4),
+    (lambda d: setattr(d, "v_head_dim", 128), 4, -4),  # D != Dv
+    (lambda d: setattr(d, "kv_dtype", 7), 4, -5),
+    (lambda d: None, 0, -6),                            # l_ext < 1
+    (lambda d: None, 5, -6),                            # ragged: q_rows != bs * (mle + 1)
+    (lambda d: d.q_stride.__setitem__(0, -1), 4, -7),
+    (lambda d: d.kbuf_stride.__setitem__(0, 257), 4, -7),   # row start not 16-B aligned
+    (lambda d: d.out_stride.__setitem__(1, 8), 4, -7),      # overlapping output rows
+    (lambda d: setattr(d, "split_tokens", 100), 4, -10),    # not a multiple of 64
+    (lambda d: (setattr(d, "split_tokens", 64), setattr(d, "n_splits", 4)), 4, -10),
+    (lambda d: setattr(d, "num_kv_indices", -1), 4, -13),
+])
+def test_invalid_descriptors_are_rejected(mutate, l_ext, code):
+    d = desc_of()
+    mutate(d)
+    assert va.verify_attn_check(d, l_ext) == code
+    assert va.lib().verify_attn_last_error().decode() != ""
+    assert va.lib().verify_attn_strerror(code).decode() not in ("", "unknown status")
+
+
+def test_null_descriptor():
+    assert va.lib().verify_attn_check(None, 4) == -1
+
+
+def test_plan_is_pure_given_cu_count():
+    d = desc_of()
+    a = va.verify_attn_plan(d, 4, 256).as_dict()
+    b = va.verify_attn_plan(d, 4, 256).as_dict()
+    assert a == b
+    assert va.verify_attn_workspace_bytes(d, 4, 256) == a["workspace_bytes"]
+
+
+def _plan_for(p: W.Problem, cus=256, **kw):
+    desc = va.make_desc(p.q.to("meta"), p.k_ext.to("meta"), p.v_ext.to("meta"), p.k_buf[:1].to("meta"),
+                        p.v_buf[:1].to("meta"), p.kv_indices.to("meta"), p.q.to("meta"), p.bs, **kw)
+    return va.verify_attn_plan(desc, p.l_ext, cus)
+
+
+def test_plan_headline_shapes():
+    # B=8, 8k prefix, l_ext=4, 16/2 heads, D=256: 2 KV heads x 65536 tokens
+    # shared over 2 resident workgroups per CU on 256 CUs -> 256-token ranges
+    meta = meta_problem(bs=8, n=8192)
+    plan = va.verify_attn_plan(va.make_desc(**meta), 4, 256)
+    assert plan.mode == 0 and plan.split_tokens == 256
+    assert plan.rows == 32 and plan.row_chunks == 1 and plan.tile_tokens == 32
+    assert plan.range_slots >= 8 * 8192 // 256
+    assert plan.workspace_bytes >= plan.range_slots * 2 * 32 * 257 * 4
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_range_slots_bound_every_ragged_batch(seed):
+    g = torch.Generator().manual_seed(seed)
+    bs = int(torch.randint(1, 40, (1,), generator=g))
+    lens = torch.randint(0, 5000, (bs,), generator=g).tolist()
+    T = sum(lens)
+    meta = meta_problem(bs=bs, l_ext=2, h_q=8, h_kv=1, d=128, n=1)
+    meta["kv_indices"] = torch.empty(T, dtype=torch.int64, device="meta")
+    for cus in (8, 80, 256):
+        plan = va.verify_attn_plan(va.make_desc(**meta), 2, cus)
+        c = plan.split_tokens
+        assert c % 64 == 0 and c >= 64
+        assert sum(math.ceil(n / c) for n in lens) <= plan.range_slots
+
+
+def test_pages_split_rule_mode():
+    plan = va.verify_attn_plan(desc_of(n_splits=8), 4, 256)
+    assert plan.mode == 1 and plan.n_splits == 8 and plan.range_slots == 3 * 8
+
+
+def test_row_chunks_beyond_64_rows():
+    plan = va.verify_attn_plan(desc_of(h_q=16, h_kv=1, l_ext=8), 8, 256)
+    assert plan.rows == 128 and plan.row_chunks == 2
+
+
+def test_run_rejects_bad_arguments_without_launching():
+    # Null pointers / bad scales return an error code; nothing is launched.
+    d = desc_of()
+    rc = va.lib().verify_attn_run(None, None, None, None, None, None, None, None, 4,
+                                  ctypes.c_float(0.1), ctypes.c_float(1.0), ctypes.c_float(1.0),
+                                  None, ctypes.byref(d), None, 0, None)
+    assert rc < 0
