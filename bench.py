@@ -1,0 +1,340 @@
+#!/usr/bin/env python3
+"""Throughput of split-KV target-verify attention on one MI355X.
+
+One step = one full pass of the hot path over one batch: the prefix kernel
+(gather + QK^T + online softmax + PV over every prefix range) and the combine
+kernel (range merge + causal draft block + final merge), launched through the
+C ABI on one stream.  Inputs are resident in HBM before timing starts.
+
+Cold cache: the K/V working set of the headline workload (134 MB) fits in the
+256 MB Infinity Cache, so the timed loop rotates over independent input
+replicas (separate pools and kv_indices); each replica was last touched
+several hundred MB of traffic earlier, so its K/V comes from HBM.  Warm-cache
+and graph-replay figures are reported beside it.
+
+Output: one JSON line on stdout (rank 0, N = 1).  ``value`` is the headline
+metric: algorithmic K/V bytes of the batch / time per step, in GB/s.
+"""
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "speculative_decoding_attention_amd", "csrc", "va_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefix_kernel_b8_8k_traffic.txt")
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--replicas", type=int, default=8,
+                    help="independent input sets rotated through the timed loop")
+    ap.add_argument("--workload", default="b8_8k")
+    ap.add_argument("--quick", action="store_true",
+                    help="headline only: no secondary workloads, no CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for name in ("va_kernels.hip", "va_internal.h", "va_api.cpp", "va_plan.cpp"):
+        with open(os.path.join(ROOT, "speculative_decoding_attention_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """HBM bytes per prefix launch from the committed counter summary, or None
+    if it is missing or was taken on a different kernel source."""
+    try:
+        fields = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    fields[k.strip()] = v.strip()
+        if fields.get("kernel_sources_sha256") != kernel_source_hash():
+            return None
+        return float(fields["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+class Runner:
+    """Pre-marshalled arguments for the two C entry points of one replica."""
+
+    def __init__(self, va, p, workspace, out):
+        import ctypes
+        self.va, self.p, self.ws, self.out = va, p, workspace, out
+        self.desc = va.make_desc(p.q, p.k_ext, p.v_ext, p.k_buf, p.v_buf, p.kv_indices, out, p.bs)
+        self.lib = va.lib()
+        F = ctypes.c_float
+        self.pre_args = (p.q.data_ptr(), p.k_buf.data_ptr(), p.v_buf.data_ptr(), p.qo_indptr.data_ptr(),
+                         p.kv_indptr.data_ptr(), p.kv_indices.data_ptr(), p.l_ext, F(p.sm_scale),
+                         F(p.k_scale), F(p.v_scale), ctypes.byref(self.desc), workspace.data_ptr(),
+                         workspace.numel())
+        self.com_args = (p.q.data_ptr(), p.k_ext.data_ptr(), p.v_ext.data_ptr(), p.qo_indptr.data_ptr(),
+                         p.kv_indptr.data_ptr(), p.l_ext, F(p.sm_scale), out.data_ptr(),
+                         ctypes.byref(self.desc), workspace.data_ptr(), workspace.numel())
+
+    def prefix(self, stream):
+        rc = self.lib.verify_attn_prefix(*self.pre_args, stream)
+        if rc:
+            raise RuntimeError("verify_attn_prefix: %d %s" % (rc, self.lib.verify_attn_last_error()))
+
+    def combine(self, stream):
+        rc = self.lib.verify_attn_combine(*self.com_args, stream)
+        if rc:
+            raise RuntimeError("verify_attn_combine: %d %s" % (rc, self.lib.verify_attn_last_error()))
+
+
+def hold_gpu(torch, ms=20.0):
+    """Keep the GPU busy for ~ms so the host can enqueue the timed launches
+    ahead of execution (the measured region then has no host gaps)."""
+    try:
+        torch.cuda._sleep(int(ms * 1e-3 * 2.4e9))
+    except Exception:
+        pass
+
+
+def time_workload(torch, va, W, name, steps, warmup, replicas, seed0=1000):
+    dev = torch.device("cuda", 0)
+    make = W.CONFIGS[name]
+    probs = [make(device=dev, seed=seed0 + r) for r in range(replicas)]
+    p0 = probs[0]
+    out = torch.empty(p0.q.shape[0], p0.h_q, p0.v_head_dim, dtype=torch.bfloat16, device=dev)
+    desc = va.make_desc(p0.q, p0.k_ext, p0.v_ext, p0.k_buf, p0.v_buf, p0.kv_indices, out, p0.bs)
+    plan = va.verify_attn_plan(desc, p0.l_ext)
+    # replicas of a ragged workload differ in length: size for the largest plan
+    ws_bytes = max(va.verify_attn_workspace_bytes(
+        va.make_desc(p.q, p.k_ext, p.v_ext, p.k_buf, p.v_buf, p.kv_indices, out, p.bs), p.l_ext)
+        for p in probs)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    runners = [Runner(va, p, ws, out) for p in probs]
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    kv_bytes = p0.kv_bytes()
+
+    def step(i):
+        r = runners[i % replicas]
+        r.prefix(sh)
+        r.combine(sh)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---- timed region: whole steps, rotating replicas (cold K/V) ----
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    hold_gpu(torch)
+    e0.record(stream)
+    for i in range(steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / steps
+
+    # ---- per-kernel durations with events on the launch stream ----
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    hold_gpu(torch)
+    for i in range(steps):
+        r = runners[i % replicas]
+        ev[i][0].record(stream)
+        r.prefix(sh)
+        ev[i][1].record(stream)
+        r.combine(sh)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    pre = [ev[i][0].elapsed_time(ev[i][1]) for i in range(steps)]
+    com = [ev[i][1].elapsed_time(ev[i][2]) for i in range(steps)]
+
+    # ---- warm cache: one replica over and over ----
+    hold_gpu(torch)
+    e0.record(stream)
+    for i in range(steps):
+        runners[0].prefix(sh)
+        runners[0].combine(sh)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_warm = e0.elapsed_time(e1) / steps
+
+    # ---- graph replay: one captured step per replica ----
+    graphs = []
+    try:
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            for r in runners:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=cap):
+                    cs = torch.cuda.current_stream().cuda_stream
+                    r.prefix(cs)
+                    r.combine(cs)
+                graphs.append(g)
+        stream.wait_stream(cap)
+        torch.cuda.synchronize()
+        for i in range(warmup):
+            graphs[i % replicas].replay()
+        torch.cuda.synchronize()
+        hold_gpu(torch)
+        e0.record(stream)
+        for i in range(steps):
+            graphs[i % replicas].replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_graph = e0.elapsed_time(e1) / steps
+    except Exception as exc:  # report, never hide
+        ms_graph = None
+        print("graph replay timing failed: %r" % (exc,), file=sys.stderr)
+
+    us = lambda ms: round(ms * 1e3, 3)
+    pre_ms = statistics.mean(pre)
+    return dict(
+        name=name, problem=p0, plan=plan.as_dict(), kv_bytes=kv_bytes,
+        ms_step=ms_step, us_step=us(ms_step), gbs=kv_bytes / (ms_step * 1e-3) / 1e9,
+        prefix_us_mean=us(pre_ms), prefix_us_median=us(statistics.median(pre)),
+        prefix_us_p10=us(sorted(pre)[len(pre) // 10]), prefix_us_p90=us(sorted(pre)[(9 * len(pre)) // 10]),
+        combine_us_mean=us(statistics.mean(com)),
+        prefix_gbs=kv_bytes / (pre_ms * 1e-3) / 1e9,
+        us_step_warm=us(ms_warm), gbs_warm=kv_bytes / (ms_warm * 1e-3) / 1e9,
+        us_step_graph=us(ms_graph) if ms_graph else None,
+        gbs_graph=(kv_bytes / (ms_graph * 1e-3) / 1e9) if ms_graph else None,
+    )
+
+
+def calibration_copy(torch):
+    """A plain device copy of exactly 1 GiB; its FETCH_SIZE / WRITE_SIZE in a
+    counter run give the scale factor for the prefix kernel's counters."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def cpu_baseline(torch, W, p_dev, min_seconds=10.0, max_passes=8):
+    """The fp64 oracle on the host cores over the whole headline batch."""
+    import oracle
+    p = p_dev.to("cpu")
+    args = (p.q, p.k_ext, p.v_ext, p.k_buf, p.v_buf, p.qo_indptr, p.kv_indptr, p.kv_indices,
+            p.sm_scale, p.k_scale, p.v_scale)
+    times = []
+    t_start = time.perf_counter()
+    while len(times) < max_passes and (time.perf_counter() - t_start) < min_seconds:
+        t0 = time.perf_counter()
+        oracle.verify_attn(*args)
+        times.append(time.perf_counter() - t0)
+    t = statistics.median(times)
+    return {
+        "value": round(p.kv_bytes() / t / 1e9, 4),
+        "unit": "GB/s",
+        "cores": oracle.max_threads(),
+        "kind": "oracle",
+        "sample": "whole headline batch (all %d sequences x %d heads), median of %d passes; %.3f s/pass"
+                  % (p.bs, p.h_q, len(times), t),
+        "us_per_call": round(t * 1e6, 1),
+    }
+
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(requested --gpus %d, WORLD_SIZE %d)" % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from speculative_decoding_attention_amd import verify_attn as va
+    from speculative_decoding_attention_amd import workloads as W
+
+    torch.cuda.set_device(0)
+    calibration_copy(torch)
+    torch.cuda.synchronize()
+    head = time_workload(torch, va, W, args.workload, args.steps, args.warmup, args.replicas)
+    print("[bench] %s: %.2f us/step (%.1f GB/s), prefix kernel %.2f us (%.1f GB/s), combine %.2f us"
+          % (head["name"], head["us_step"], head["gbs"], head["prefix_us_mean"], head["prefix_gbs"],
+             head["combine_us_mean"]), file=sys.stderr, flush=True)
+
+    secondary = {}
+    if not args.quick:
+        for name, reps in (("b4_64k", 1), ("fp8_ragged", 8)):
+            r = time_workload(torch, va, W, name, max(20, args.steps // 4), 5, reps, seed0=2000)
+            secondary[name] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in r.items()
+                               if k not in ("problem", "name")}
+            print("[bench] %s: %.2f us/step (%.1f GB/s), prefix %.2f us (%.1f GB/s)"
+                  % (name, r["us_step"], r["gbs"], r["prefix_us_mean"], r["prefix_gbs"]),
+                  file=sys.stderr, flush=True)
+            del r
+            torch.cuda.empty_cache()
+
+    cpu = None
+    if not (args.quick or args.no_cpu_baseline):
+        cpu = cpu_baseline(torch, W, head["problem"])
+        print("[bench] cpu oracle: %s" % json.dumps(cpu), file=sys.stderr, flush=True)
+
+    p = head["problem"]
+    traffic = recorded_traffic()
+    achieved = head["prefix_gbs"]
+    line = {
+        "metric": "verify-attn achieved HBM GB/s and us/call (B=8, 8k prefix, l_ext=4, D=256)",
+        "value": round(head["gbs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_step"], 6),
+        "us_per_call": head["us_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "b8_8k: B=8, prefix 8192 each, l_ext=4, h_q=16, h_kv=2, D=Dv=256, bf16 pool "
+                        "(2x needed rows, scattered kv_indices), k_scale=0.5, v_scale=0.25",
+            "batch": p.bs, "prefix": p.prefix_lens[0], "l_ext": p.l_ext, "h_q": p.h_q,
+            "h_kv": p.h_kv, "head_dim": p.head_dim, "kv_bytes": head["kv_bytes"],
+            "cache": "cold (rotating %d replicas)" % args.replicas,
+            "plan": head["plan"],
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": "prefix_kernel<bf16, D=256, MB=2>",
+            "kernel_us": head["prefix_us_mean"],
+        },
+        "cpu_baseline": cpu,
+        "detail": {
+            "prefix_us": {"mean": head["prefix_us_mean"], "median": head["prefix_us_median"],
+                          "p10": head["prefix_us_p10"], "p90": head["prefix_us_p90"]},
+            "combine_us_mean": head["combine_us_mean"],
+            "warm_cache": {"us_per_call": head["us_step_warm"], "gbs": round(head["gbs_warm"], 2)},
+            "graph_replay": {"us_per_call": head["us_step_graph"],
+                             "gbs": round(head["gbs_graph"], 2) if head["gbs_graph"] else None},
+            "secondary": secondary,
+        },
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

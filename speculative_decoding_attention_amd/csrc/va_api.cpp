@@ -83,9 +83,9 @@ int prefix_impl(const void *q, const void *k_buf, const void *v_buf, const int32
     const int eb = desc->kv_dtype == VA_DTYPE_FP8_E4M3FN ? 1 : 2;
     p.q_s0 = desc->q_stride[0];
     p.q_s1 = desc->q_stride[1];
-    p.kb_s0 = desc->kbuf_stride[0] * eb;
+    p.kb_s0 = (uint32_t)(desc->kbuf_stride[0] * eb);
     p.kb_s1 = desc->kbuf_stride[1] * eb;
-    p.vb_s0 = desc->vbuf_stride[0] * eb;
+    p.vb_s0 = (uint32_t)(desc->vbuf_stride[0] * eb);
     p.vb_s1 = desc->vbuf_stride[1] * eb;
     p.qk_scale_log2 = (float)((double)sm_scale * (double)k_scale * 1.4426950408889634);
     p.v_scale = v_scale;
@@ -98,8 +98,8 @@ int prefix_impl(const void *q, const void *k_buf, const void *v_buf, const int32
     p.mode = plan.mode;
     p.split_tokens = plan.split_tokens > 0 ? plan.split_tokens : 1;
     p.n_splits = plan.n_splits > 0 ? plan.n_splits : 1;
-    const int mb = row_blocks_for(plan.rows < kRowChunk ? plan.rows : kRowChunk);
-    int e = launch_prefix(p, desc->head_dim, desc->kv_dtype == VA_DTYPE_FP8_E4M3FN, mb,
+    const int qb = query_blocks_for(plan.rows < kRowChunk ? plan.rows : kRowChunk);
+    int e = launch_prefix(p, desc->head_dim, desc->kv_dtype == VA_DTYPE_FP8_E4M3FN, qb,
                           plan.prefix_blocks, stream);
     if (e != 0) {
         set_error("prefix kernel launch: %s", hip_error_string(e));

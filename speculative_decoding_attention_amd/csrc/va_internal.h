@@ -10,27 +10,29 @@
 namespace va {
 
 // Rows of one KV head's query tile are processed in chunks of at most this
-// many rows (4 MFMA row blocks of 16).
+// many rows (2 MFMA column blocks of 32).
 constexpr int kRowChunk = 64;
 // Granule of the pages' equal-split rule (ranges are rounded up to it).
 constexpr int kEvenSplitGranule = 32;
 // Threads per workgroup of both kernels (4 wavefronts of 64).
 constexpr int kThreads = 256;
-// Prefix kernel workgroups resident per CU the split heuristic aims for.
-constexpr int kResidentPerCU = 2;
+// Depth of the prefix kernel's LDS ring of K/V tiles (<= 32 KB per tile) and
+// the workgroups per CU that leaves room for in 160 KB of LDS; the split
+// heuristic aims for that many resident workgroups per CU.
+constexpr int kRingStages = 2;
+constexpr int kResidentPerCU = kRingStages == 2 ? 2 : 1;
 // Smallest range the heuristic chooses; ranges are multiples of this.
 constexpr int kSplitQuantum = 64;
 
-// Prefix tokens per LDS tile: a D=256 tile of 32 tokens holds 32 KB of K+V in
-// bf16, a D<=128 tile 64 tokens (<= 32 KB).
-constexpr int tile_tokens_for(int head_dim) { return head_dim == 256 ? 32 : 64; }
-
-// 16-row MFMA blocks per row chunk (1, 2 or 4).
-inline int row_blocks_for(int rows_in_chunk)
+// Prefix tokens per LDS tile: as many as keep K+V of one tile within 32 KB of
+// raw pool bytes, at most 128 (bf16 D=256: 32; fp8 D=128: 128).
+constexpr int tile_tokens_for(int head_dim, int elem_bytes)
 {
-    int mb = (rows_in_chunk + 15) / 16;
-    return mb <= 1 ? 1 : (mb <= 2 ? 2 : 4);
+    return 16384 / (head_dim * elem_bytes) > 128 ? 128 : 16384 / (head_dim * elem_bytes);
 }
+
+// 32-row query blocks (MFMA column blocks) per row chunk: 1 or 2.
+inline int query_blocks_for(int rows_in_chunk) { return rows_in_chunk <= 32 ? 1 : 2; }
 
 struct PrefixParams {
     const uint16_t *q;
@@ -42,8 +44,8 @@ struct PrefixParams {
     float *part_o;    // [range_slots * h_kv, rows, D] fp32
     float *part_lse;  // [range_slots * h_kv, rows]    fp32 (natural log)
     int64_t q_s0, q_s1;        // elements
-    int64_t kb_s0, kb_s1;      // bytes
-    int64_t vb_s0, vb_s1;      // bytes
+    uint32_t kb_s0, vb_s0;     // pool row strides, bytes (< 2^32, checked on the host)
+    int64_t kb_s1, vb_s1;      // pool head strides, bytes
     float qk_scale_log2;       // sm_scale * k_scale * log2(e)
     float v_scale;
     int32_t bs, h_kv, group, l_ext, rows, row_chunks;
@@ -66,7 +68,7 @@ struct CombineParams {
 };
 
 // Launchers (defined in va_kernels.hip).  Return a hipError_t value.
-int launch_prefix(const PrefixParams &p, int head_dim, bool kv_fp8, int row_blocks,
+int launch_prefix(const PrefixParams &p, int head_dim, bool kv_fp8, int qblocks,
                   int64_t blocks, void *stream);
 int launch_combine(const CombineParams &p, int head_dim, int64_t blocks, void *stream);
 const char *hip_error_string(int err);

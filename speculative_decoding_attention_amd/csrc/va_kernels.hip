@@ -22,6 +22,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "va_internal.h"
 
 namespace va {
@@ -30,6 +32,8 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -76,30 +80,6 @@ __device__ __forceinline__ float round_to_e4m3(float x)
         r = ldexpf(rintf(ldexpf(a, 4 - e)), e - 4);
     }
     return copysignf(r, x);
-}
-
-__device__ __forceinline__ u32x4_t fp8x16_to_bf16_lo(u32x4_t v)
-{
-    u32x4_t o;
-#pragma unroll
-    for (int w = 0; w < 2; ++w) {
-        const uint32_t x = v[w];
-        o[2 * w + 0] = e4m3_to_bf16(x & 0xffu) | (e4m3_to_bf16((x >> 8) & 0xffu) << 16);
-        o[2 * w + 1] = e4m3_to_bf16((x >> 16) & 0xffu) | (e4m3_to_bf16(x >> 24) << 16);
-    }
-    return o;
-}
-
-__device__ __forceinline__ u32x4_t fp8x16_to_bf16_hi(u32x4_t v)
-{
-    u32x4_t o;
-#pragma unroll
-    for (int w = 0; w < 2; ++w) {
-        const uint32_t x = v[2 + w];
-        o[2 * w + 0] = e4m3_to_bf16(x & 0xffu) | (e4m3_to_bf16((x >> 8) & 0xffu) << 16);
-        o[2 * w + 1] = e4m3_to_bf16((x >> 16) & 0xffu) | (e4m3_to_bf16(x >> 24) << 16);
-    }
-    return o;
 }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
@@ -200,44 +180,160 @@ __device__ __forceinline__ void ranges_of(const int32_t *kv_indptr, int32_t bs, 
 }
 
 // ----------------------------------------------------------- prefix kernel ---
-// LDS tile layouts (bf16 rows of D elements, 16-byte chunks):
-//   K: chunk c of token row t lives at chunk c ^ (t & 7) -- the score MFMA
-//      reads 16 consecutive rows at one chunk, which this spreads over banks;
-//   V: chunk c of token row t lives at chunk c ^ (((t >> 2) & 3) << 1) -- the
-//      transposed 16-bit reads of the value MFMA touch rows 4 apart.
-// P tile: for value step ks (32 tokens) and row block rb, lane l's 8 bf16
-// B-operand values sit at ((ks * MB + rb) * 64 + l) * 16.
-template <bool FP8, int D, int MB>
+// Asynchronous global -> LDS copies.  global_load_lds_dwordx{1,4} writes lane
+// l's 4 / 16 bytes to LDS at M0 + 4l / 16l and counts in vmcnt like any load
+// (loads retire in issue order).  They are issued from inline asm so that the
+// compiler inserts no waits of its own for them; every wait is explicit.
+__device__ __forceinline__ uint32_t lds_offset(const void *p) { return (uint32_t)(uintptr_t)p; }
+
+__device__ __forceinline__ void dma16(const void *g, uint32_t lds_base)
+{
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :: "s"(lds_base), "v"(g) : "memory", "m0");
+}
+
+__device__ __forceinline__ void dma4(const void *g, uint32_t lds_base)
+{
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+                 :: "s"(lds_base), "v"(g) : "memory", "m0");
+}
+
+// Wait until at most N vector-memory loads of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+// Workgroup barrier for LDS data only: this wave's LDS operations are complete
+// (lgkmcnt 0) before it arrives.  Copies into LDS are covered by wait_vm first.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+__device__ __forceinline__ u32x4_t fp8x8_to_bf16(u32x2_t v)
+{
+    u32x4_t o;
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+        const uint32_t x = v[w];
+        o[2 * w + 0] = e4m3_to_bf16(x & 0xffu) | (e4m3_to_bf16((x >> 8) & 0xffu) << 16);
+        o[2 * w + 1] = e4m3_to_bf16((x >> 16) & 0xffu) | (e4m3_to_bf16(x >> 24) << 16);
+    }
+    return o;
+}
+
+template <bool FP8, int D>
+struct PrefixGeom {
+    static constexpr int E = FP8 ? 1 : 2;               // pool bytes per element
+    static constexpr int ROWB = D * E;                  // pool bytes per K (or V) row
+    static constexpr int TN0 = 16384 / ROWB;
+    static constexpr int TN = TN0 > 128 ? 128 : TN0;    // tokens per tile (K+V <= 32 KB)
+    static constexpr int LCH = ROWB / 16;               // 16-byte chunks per row
+    static constexpr int RPI = 64 / LCH;                // rows per wave-wide copy
+    static constexpr int NBUF = kRingStages;            // tiles in the LDS ring
+    static constexpr int STAGE_K = TN * ROWB;
+    static constexpr int STAGE = 2 * STAGE_K;           // K tile then V tile
+    static constexpr int NIKW = TN * LCH / 256;         // K copies per wave per tile (V: same)
+    static constexpr int RW = NIKW * RPI;               // rows each wave copies per tile
+    static constexpr int NIDX = 3;                      // index slots per wave
+    static_assert(NIKW >= 1 && NIKW * 256 == TN * LCH, "tile / copy geometry");
+    static_assert(2 * RW <= 64, "one index copy per wave per tile");
+    static_assert(TN == tile_tokens_for(D, E), "host and kernel tile rules agree");
+};
+
+// LDS layouts (per ring stage; rows of raw pool bytes, 16-byte chunks):
+//   K: chunk c of token row t sits at chunk c ^ kswz(t), kswz(t) = t & 15 (t & 7
+//      for 8-chunk rows): the score MFMA reads 16 consecutive rows at one
+//      chunk per LDS cycle, which this puts on 16 different bank groups;
+//   V: chunk c of token row t sits at chunk c ^ vswz(t).  bf16 values are read
+//      with the 16-bit transposing read: 32 lanes cover 4 consecutive rows x 4
+//      chunks, so vswz(t) = (t & 3) << 2 moves each row to its own group of 4
+//      chunks ((t & 1) << 2 for 8-chunk rows); fp8 values are read byte by
+//      byte, vswz(t) = (t >> 2) & 3.
+// The copies choose, for every LDS chunk, the pool chunk that belongs there.
+//
+// Work split: every wave computes the scores of all query rows of a 32-token
+// sub-tile (v_mfma_f32_32x32x16: tokens x 32 query rows), keeps its own copy
+// of the running max / sum, and accumulates only its share of the output
+// columns.  The score C-layout of one 32 x 32 block is exactly the B operand
+// of two value MFMA k-steps, so probabilities never leave registers and a
+// tile needs a single barrier.  The running max is raised only when a row's
+// new maximum exceeds it by more than 2^8 (the rescale of the accumulators is
+// then skipped for most tiles); probabilities stay below 2^8, far inside the
+// range of bf16 and fp32.
+__device__ __forceinline__ f32x16_t mfma32x32x16(bf16x8_t a, bf16x8_t b, f32x16_t c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16_t mfma32x32x16_fp8(uint64_t a, uint64_t b, f32x16_t c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8((long)a, (long)b, c, 0, 0, 0);
+}
+
+// value of lane l ^ 32
+__device__ __forceinline__ float swap_halves(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+}
+
+// E4M3FN code of a value that is already exactly representable (|v| <= 448).
+__device__ __forceinline__ uint32_t e4m3_code(float v)
+{
+    const uint32_t u = __float_as_uint(v);
+    const uint32_t s = (u >> 24) & 0x80u;
+    const float a = fabsf(v);
+    uint32_t c;
+    if (a >= 0x1p-6f)
+        c = ((((u >> 23) & 0xffu) - 120u) << 3) | ((u >> 20) & 7u);  // exponent bias 127 -> 7
+    else
+        c = (uint32_t)(a * 512.0f);                                   // subnormal: m * 2^-9
+    return s | c;
+}
+
+template <bool FP8, int D, int NQB>
 __global__ __launch_bounds__(kThreads) void prefix_kernel(const PrefixParams p)
 {
-    constexpr int TN = tile_tokens_for(D);
-    constexpr int E = FP8 ? 1 : 2;          // pool bytes per element
-    constexpr int GCH = D * E / 16;         // 16-byte chunks per pool row
-    constexpr int ROWB = D * 2;             // LDS bytes per bf16 row
-    constexpr int CPT = TN * GCH / kThreads;  // staged chunks per thread per tile
-    constexpr int RSTEP = kThreads / GCH;   // row step between a thread's chunks
-    constexpr int NTB = TN / 16;            // 16-token score blocks per tile
-    constexpr int NKS_QK = D / 32;          // k-steps of the score MFMA
-    constexpr int NKS_PV = TN / 32;         // k-steps of the value MFMA
-    constexpr int NP = NTB * MB;            // score blocks per tile
-    constexpr int PPW = NP >= 4 ? NP / 4 : 1;  // score blocks per wave
-    constexpr int QKW = NP >= 4 ? 4 : NP;   // waves that compute scores
-    constexpr int DW = D / 4;               // output columns per wave
-    constexpr int DB = DW / 16;             // 16-column blocks per wave
-    static_assert(CPT >= 1 && CPT * kThreads == TN * GCH, "tile/thread mismatch");
-    static_assert(MB == 1 || MB == 2 || MB == 4, "row blocks");
+    using G = PrefixGeom<FP8, D>;
+    constexpr int TN = G::TN;
+    constexpr int ROWB = G::ROWB;
+    constexpr int LCH = G::LCH;
+    constexpr int NBUF = G::NBUF;
+    constexpr int NIKW = G::NIKW;
+    constexpr int RW = G::RW;
+    constexpr int NKS = D / 16;             // k-steps of the score MFMA
+    constexpr int NSUB = TN / 32;           // 32-token sub-tiles per tile
+    constexpr int NPVW = D >= 128 ? 4 : D / 32;  // waves that own output columns
+    constexpr int DWV = D / NPVW;           // output columns per such wave
+    constexpr int DBW = DWV / 32;           // 32-column blocks per such wave
+    constexpr int KSWZ = (LCH < 16 ? LCH : 16) - 1;
+    constexpr int VSWZ_ROWS = LCH >= 16 ? 3 : 1;  // bf16: rows whose 4-chunk groups differ
+    constexpr float kRescale = 8.0f;        // log2 headroom before the max is raised
+    static_assert(NQB == 1 || NQB == 2, "query blocks");
+    static_assert(NQB * 32 * D * 2 <= G::STAGE, "query tile fits one ring stage");
+    static_assert(TN % 32 == 0 && DWV % 32 == 0, "tile / column geometry");
+    // after tile t's copies, the next two steps issue 2 index copies and up to
+    // 2 * 2 * NIKW tile copies
+    constexpr int VM_TWO_AHEAD = 2 + 4 * NIKW;
+    constexpr int VM_ONE_AHEAD = 2 + 2 * NIKW;
+    constexpr int VM_NONE_AHEAD = 2;
 
-    __shared__ __attribute__((aligned(16))) uint8_t s_k[2][TN * ROWB];
-    __shared__ __attribute__((aligned(16))) uint8_t s_v[2][TN * ROWB];
-    __shared__ __attribute__((aligned(16))) uint8_t s_p[NKS_PV * MB * 64 * 16];
-    __shared__ float s_max[4][16];
-    __shared__ float s_sum[4][16];
+    __shared__ __attribute__((aligned(1024))) uint8_t s_ring[NBUF * G::STAGE];
+    __shared__ __attribute__((aligned(16))) int64_t s_idx[4][G::NIDX][RW];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int col = lane & 15;
-    const int grp = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31;   // token (A) / query row (B, C) within a 32 block
+    const int half = lane >> 5;  // k half of the operands
 
     // ---- work item: (range, KV head, row chunk) ----
     const int64_t blk = blockIdx.x;
@@ -257,7 +353,7 @@ __global__ __launch_bounds__(kThreads) void prefix_kernel(const PrefixParams p)
     if (rg.start >= rg.end) {
         // Empty range: output 0 and log-sum-exp -inf, so the merge weight is
         // exactly 0 and no stale value can leak in.
-        const int nr = min(rows - row0, MB * 16);
+        const int nr = min(rows - row0, NQB * 32);
         for (int e = tid; e < nr * D; e += kThreads)
             po[(int64_t)(row0 + e / D) * D + (e % D)] = 0.0f;
         if (tid < nr)
@@ -269,266 +365,346 @@ __global__ __launch_bounds__(kThreads) void prefix_kernel(const PrefixParams p)
     const int len = rg.end - rg.start;
     const int nt = (len + TN - 1) / TN;
     const int qo = p.qo_indptr[rg.b];
+    const uint32_t ring = lds_offset(s_ring);
 
-    // ---- this wave's score blocks and its query operand ----
-    const int pair0 = wave * PPW;
-    const int rbw = pair0 / NTB;  // row block of this wave's score blocks
-    const int tb0 = pair0 % NTB;  // first token block
-    const bool qk_active = wave < QKW;
-    bf16x8_t qreg[NKS_QK];
+    // ---- query tile -> ring stage NBUF-1 (bf16 rows of D, row-major) ----
     {
-        const int r = row0 + rbw * 16 + col;
-        const bool rv = qk_active && r < rows;
-        const int hg = rv ? r / p.l_ext : 0;
-        const int di = rv ? r % p.l_ext : 0;
-        const uint16_t *qrow = p.q + (int64_t)(qo + di) * p.q_s0 + (int64_t)(kvh * p.group + hg) * p.q_s1;
+        constexpr int QCH = D / 8;                    // 16-byte chunks per query row
+        constexpr int QI = NQB * 32 * QCH / 64;       // wave-wide copies for the tile
+        for (int i = wave; i < QI; i += 4) {
+            const int e = i * 64 + lane;
+            const int r = row0 + e / QCH;             // query row of this chunk
+            const int rr = r < rows ? r : row0;       // padding rows copy a valid row
+            const int hg = rr / p.l_ext, di = rr % p.l_ext;
+            const uint16_t *src = p.q + (int64_t)(qo + di) * p.q_s0 +
+                                  (int64_t)(kvh * p.group + hg) * p.q_s1 + (e % QCH) * 8;
+            dma16(src, __builtin_amdgcn_readfirstlane(ring + (NBUF - 1) * G::STAGE + i * 1024));
+        }
+    }
+
+    // ---- copy issue: index slots and K/V tiles ----
+    const uint32_t idx_base = lds_offset(&s_idx[wave][0][0]);
+    auto issue_idx = [&](int k) {
+        // rows wave*RW .. +RW of tile k; tokens past the range re-read the last
+        // token (in bounds, and masked out of the scores)
+        if (lane < 2 * RW) {
+            int tok = k * TN + wave * RW + (lane >> 1);
+            tok = tok < len ? tok : len - 1;
+            const uint32_t *src = (const uint32_t *)(p.kv_indices + kv0 + tok) + (lane & 1);
+            dma4(src, __builtin_amdgcn_readfirstlane(idx_base + (k % G::NIDX) * RW * 8));
+        }
+    };
+    const uint8_t *kbase = p.k_buf + (int64_t)kvh * p.kb_s1;
+    const uint8_t *vbase = p.v_buf + (int64_t)kvh * p.vb_s1;
+    auto issue_tile = [&](int k) {
+        const int64_t *ix = &s_idx[wave][k % G::NIDX][0];
+        const uint32_t st = ring + (k % NBUF) * G::STAGE + wave * NIKW * 1024;
 #pragma unroll
-        for (int ks = 0; ks < NKS_QK; ++ks) {
-            u32x4_t raw = {0u, 0u, 0u, 0u};
-            if (rv)
-                raw = *(const u32x4_t *)(qrow + ks * 32 + grp * 8);
-            if (FP8) {
+        for (int i = 0; i < NIKW; ++i) {
+            const int rl = i * G::RPI + lane / LCH;   // row within this wave's rows
+            const int row = wave * RW + rl;           // row within the tile
+            const int pc = lane % LCH;                // LDS chunk within the row
+            const int vz = FP8 ? ((row >> 2) & 3) : ((row & VSWZ_ROWS) << 2);
+            const uint64_t t = (uint64_t)ix[rl];
+            dma16(kbase + t * p.kb_s0 + ((pc ^ (row & KSWZ)) << 4),
+                  __builtin_amdgcn_readfirstlane(st + i * 1024));
+            dma16(vbase + t * p.vb_s0 + ((pc ^ vz) << 4),
+                  __builtin_amdgcn_readfirstlane(st + G::STAGE_K + i * 1024));
+        }
+    };
+
+    // prologue: steps j = 0 .. NBUF-2, step j = [index copy of tile j+2][tile j].
+    // Loads retire in order, so "index slot j has landed" is "at most the
+    // loads issued after it are outstanding": 2 index copies for j = 0, then
+    // one tile more per step up to the steady-state count.
+    static_assert(NBUF == 2 || NBUF == 4, "wait counts are written for 2- or 4-stage rings");
+    issue_idx(0);
+    issue_idx(1);
+    issue_idx(2);
+    wait_vm<2>();
+    issue_tile(0);
+    if constexpr (NBUF == 4) {
+        issue_idx(3);
+        if (1 < nt) {
+            wait_vm<2 * NIKW + 2>();
+            issue_tile(1);
+        }
+        issue_idx(4);
+        if (2 < nt) {
+            wait_vm<4 * NIKW + 2>();
+            issue_tile(2);
+        }
+        // the query tile was copied before all of that: 5 index copies and
+        // min(nt, 3) tiles came after it
+        if (nt >= 3)
+            wait_vm<5 + 6 * NIKW>();
+        else if (nt == 2)
+            wait_vm<5 + 4 * NIKW>();
+        else
+            wait_vm<5 + 2 * NIKW>();
+    } else {
+        wait_vm<3 + 2 * NIKW>();  // after the query tile: 3 index copies and tile 0
+    }
+    lds_barrier();
+
+    // ---- query operand (B: col = query row, k = d): bf16 or E4M3FN codes ----
+    typedef typename std::conditional<FP8, uint64_t, bf16x8_t>::type qop_t;
+    qop_t qreg[NQB][NKS];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+        const int rl = qb * 32 + l32;
+        const bool rv = row0 + rl < rows;
+        const uint8_t *qrow = s_ring + (NBUF - 1) * G::STAGE + (rv ? rl : 0) * D * 2;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            u32x4_t raw = *(const u32x4_t *)(qrow + (ks * 2 + half) * 16);
+            if (!rv)
+                raw = u32x4_t{0u, 0u, 0u, 0u};
+            if constexpr (FP8) {
                 // the prefix dot product uses q rounded to the pool dtype
+                uint64_t codes = 0;
 #pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    const uint32_t lo = f32_to_bf16_rne(round_to_e4m3(bf16_to_f32(raw[w] & 0xffffu)));
-                    const uint32_t hi = f32_to_bf16_rne(round_to_e4m3(bf16_to_f32(raw[w] >> 16)));
-                    raw[w] = lo | (hi << 16);
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t h = (raw[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+                    codes |= (uint64_t)e4m3_code(round_to_e4m3(bf16_to_f32(h))) << (8 * e);
                 }
+                qreg[qb][ks] = codes;
+            } else {
+                qreg[qb][ks] = as_bf16x8(raw);
             }
-            qreg[ks] = as_bf16x8(raw);
         }
     }
 
-    // ---- staging: this thread's rows and chunk of every tile ----
-    const int s_ch = tid % GCH;
-    const int s_row0 = tid / GCH;
-    const uint8_t *kbase = p.k_buf + (int64_t)kvh * p.kb_s1 + s_ch * 16;
-    const uint8_t *vbase = p.v_buf + (int64_t)kvh * p.vb_s1 + s_ch * 16;
-    u32x4_t stk[CPT], stv[CPT];
-    int64_t sidx[CPT];
-
-    auto load_idx = [&](int t) {
+    // ---- running state: lane's query row in block qb is 32*qb + l32 ----
+    float m_ref[NQB], l_part[NQB];
+    f32x16_t oacc[DBW][NQB];
 #pragma unroll
-        for (int j = 0; j < CPT; ++j) {
-            const int tok = t * TN + s_row0 + j * RSTEP;
-            sidx[j] = (t < nt && tok < len) ? p.kv_indices[kv0 + tok] : -1;
-        }
-    };
-    auto load_data = [&]() {
+    for (int qb = 0; qb < NQB; ++qb) {
+        m_ref[qb] = -INFINITY;
+        l_part[qb] = 0.0f;
 #pragma unroll
-        for (int j = 0; j < CPT; ++j) {
-            if (sidx[j] >= 0) {
-                stk[j] = *(const u32x4_t *)(kbase + sidx[j] * p.kb_s0);
-                stv[j] = *(const u32x4_t *)(vbase + sidx[j] * p.vb_s0);
-            } else {
-                stk[j] = u32x4_t{0u, 0u, 0u, 0u};
-                stv[j] = u32x4_t{0u, 0u, 0u, 0u};
-            }
-        }
-    };
-    auto store_tile = [&](int buf) {
-#pragma unroll
-        for (int j = 0; j < CPT; ++j) {
-            const int row = s_row0 + j * RSTEP;
-            uint8_t *kr = s_k[buf] + row * ROWB;
-            uint8_t *vr = s_v[buf] + row * ROWB;
-            const int kz = row & 7;
-            const int vz = ((row >> 2) & 3) << 1;
-            if (FP8) {
-                const int c0 = 2 * s_ch, c1 = 2 * s_ch + 1;
-                *(u32x4_t *)(kr + ((c0 ^ kz) << 4)) = fp8x16_to_bf16_lo(stk[j]);
-                *(u32x4_t *)(kr + ((c1 ^ kz) << 4)) = fp8x16_to_bf16_hi(stk[j]);
-                *(u32x4_t *)(vr + ((c0 ^ vz) << 4)) = fp8x16_to_bf16_lo(stv[j]);
-                *(u32x4_t *)(vr + ((c1 ^ vz) << 4)) = fp8x16_to_bf16_hi(stv[j]);
-            } else {
-                *(u32x4_t *)(kr + ((s_ch ^ kz) << 4)) = stk[j];
-                *(u32x4_t *)(vr + ((s_ch ^ vz) << 4)) = stv[j];
-            }
-        }
-    };
-
-    // ---- running softmax state (lane's row in each row block: 16*rb + col) ----
-    float m_run[MB], l_run[MB];
-    f32x4_t oacc[DB][MB];
-#pragma unroll
-    for (int rb = 0; rb < MB; ++rb) {
-        m_run[rb] = -INFINITY;
-        l_run[rb] = 0.0f;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-            oacc[db][rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int db = 0; db < DBW; ++db)
+            oacc[db][qb] = f32x16_t{};
     }
-
-    // prologue: tile 0 into LDS, tile 1 in flight, indices of tile 2 loaded
-    load_idx(0);
-    load_data();
-    store_tile(0);
-    load_idx(1);
-    load_data();
-    load_idx(2);
-    __syncthreads();
+    const bool pv_wave = wave < NPVW;
 
     const float qk_scale = p.qk_scale_log2;
     for (int t = 0; t < nt; ++t) {
-        const int buf = t & 1;
-        const uint8_t *K = s_k[buf];
-        const uint8_t *V = s_v[buf];
+        // tile t's copies by this wave are complete; then everyone's are
+        if constexpr (NBUF == 4) {
+            const int after = nt - 1 - t;
+            if (after >= 2)
+                wait_vm<VM_TWO_AHEAD>();
+            else if (after == 1)
+                wait_vm<VM_ONE_AHEAD>();
+            else
+                wait_vm<VM_NONE_AHEAD>();
+        } else {
+            wait_vm<0>();  // tile t was the last copy issued
+        }
+        lds_barrier();
 
-        // ---- scores of this wave's blocks: S^T[token][row] ----
-        f32x4_t sc[PPW];
-        if (qk_active) {
-            float lmax = -INFINITY;
-#pragma unroll
-            for (int pp = 0; pp < PPW; ++pp) {
-                const int tb = tb0 + pp;
-                const int krow = tb * 16 + col;
-                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < NKS_QK; ++ks) {
-                    const int ch = (ks * 4 + grp) ^ (krow & 7);
-                    const u32x4_t a = *(const u32x4_t *)(K + krow * ROWB + (ch << 4));
-                    acc = mfma16x16x32(as_bf16x8(a), qreg[ks], acc);
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int tok = t * TN + tb * 16 + grp * 4 + i;
-                    const float v = tok < len ? acc[i] * qk_scale : -INFINITY;
-                    acc[i] = v;
-                    lmax = fmaxf(lmax, v);
-                }
-                sc[pp] = acc;
+        // step j = t + NBUF - 1 into the stage tile t-1 used (everyone is past it)
+        {
+            const int j = t + NBUF - 1;
+            issue_idx(j + 2);
+            if (j < nt) {
+                wait_vm<4 * NIKW + 2>();  // index slot j, copied two steps ago
+                issue_tile(j);
             }
-            lmax = fmaxf(lmax, __shfl_xor(lmax, 16));
-            lmax = fmaxf(lmax, __shfl_xor(lmax, 32));
-            if (grp == 0)
-                s_max[wave][col] = lmax;
-        }
-        __syncthreads();
-
-        // ---- tile max per row, running-state rescale factors ----
-        float alpha[MB];
-        float m_w = 0.0f;  // new running max of this wave's score row block
-#pragma unroll
-        for (int rb = 0; rb < MB; ++rb) {
-            float mt = -INFINITY;
-#pragma unroll
-            for (int w = 0; w < QKW; ++w)
-                if ((w * PPW) / NTB == rb)
-                    mt = fmaxf(mt, s_max[w][col]);
-            const float mn = fmaxf(m_run[rb], mt);
-            alpha[rb] = exp2f(m_run[rb] - mn);
-            m_run[rb] = mn;
-            if (rb == rbw)
-                m_w = mn;
         }
 
-        // ---- probabilities (bf16) into LDS, partial row sums ----
-        if (qk_active) {
-            float lsum = 0.0f;
+        const uint8_t *K = s_ring + (t % NBUF) * G::STAGE;
+        const uint8_t *V = K + G::STAGE_K;
+
+        // one 32-token sub-tile; tokens past the range are masked only in the
+        // (at most one) sub-tile that straddles the end
+        auto sub_tile = [&](const int sub, auto masked) {
+            const int tok0 = t * TN + sub * 32;  // first token of the sub-tile
+
+            // ---- scores S^T[token][query row], 32 x 32 per query block ----
+            // two accumulators per block (even / odd k-steps) halve the chain of
+            // dependent MFMAs
+            f32x16_t sc[NQB], sc2[NQB];
 #pragma unroll
-            for (int pp = 0; pp < PPW; ++pp) {
-                const int tb = tb0 + pp;
-                uint32_t h[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    h[i] = f32_to_bf16_rne(exp2f(sc[pp][i] - m_w));
-                    lsum += bf16_to_f32(h[i]);
-                }
-                const u32x2_t w2 = {h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-                *(u32x2_t *)(s_p + (((tb >> 1) * MB + rbw) * 64 + lane) * 16 + (tb & 1) * 8) = w2;
+            for (int qb = 0; qb < NQB; ++qb) {
+                sc[qb] = f32x16_t{};
+                sc2[qb] = f32x16_t{};
             }
-            lsum += __shfl_xor(lsum, 16);
-            lsum += __shfl_xor(lsum, 32);
-            if (grp == 0)
-                s_sum[wave][col] = lsum;
-        }
-        __syncthreads();
-
-        // ---- O^T[dv][row] = alpha * O^T + V^T P^T over this wave's columns ----
+            const int krow = sub * 32 + l32;
 #pragma unroll
-        for (int rb = 0; rb < MB; ++rb) {
-            float ts = 0.0f;
+            for (int ks = 0; ks < NKS; ++ks) {
+                if constexpr (FP8) {
+                    const int ch = ks ^ (krow & KSWZ);
+                    const uint64_t a = *(const uint64_t *)(K + krow * ROWB + (ch << 4) + half * 8);
 #pragma unroll
-            for (int w = 0; w < QKW; ++w)
-                if ((w * PPW) / NTB == rb)
-                    ts += s_sum[w][col];
-            l_run[rb] = l_run[rb] * alpha[rb] + ts;
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-                oacc[db][rb] *= alpha[rb];
-        }
-#pragma unroll
-        for (int ks = 0; ks < NKS_PV; ++ks) {
-            bf16x8_t pb[MB];
-#pragma unroll
-            for (int rb = 0; rb < MB; ++rb)
-                pb[rb] = as_bf16x8(*(const u32x4_t *)(s_p + ((ks * MB + rb) * 64 + lane) * 16));
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const int dv = wave * DW + db * 16 + col;
-                const int cch = dv >> 3;
-                const int cin = (dv & 7) * 2;
-                uint32_t w4[4];
-#pragma unroll
-                for (int i2 = 0; i2 < 4; ++i2) {
-                    uint32_t pair = 0;
-#pragma unroll
-                    for (int hh = 0; hh < 2; ++hh) {
-                        const int i = 2 * i2 + hh;
-                        const int tok = ks * 32 + (i >> 2) * 16 + grp * 4 + (i & 3);
-                        const int pc = cch ^ (((tok >> 2) & 3) << 1);
-                        const uint32_t v = *(const uint16_t *)(V + tok * ROWB + (pc << 4) + cin);
-                        pair |= v << (16 * hh);
+                    for (int qb = 0; qb < NQB; ++qb) {
+                        if (ks & 1)
+                            sc2[qb] = mfma32x32x16_fp8(a, qreg[qb][ks], sc2[qb]);
+                        else
+                            sc[qb] = mfma32x32x16_fp8(a, qreg[qb][ks], sc[qb]);
                     }
-                    w4[i2] = pair;
-                }
-                const bf16x8_t a = as_bf16x8(u32x4_t{w4[0], w4[1], w4[2], w4[3]});
+                } else {
+                    const int ch = (ks * 2 + half) ^ (krow & KSWZ);
+                    const bf16x8_t a = as_bf16x8(*(const u32x4_t *)(K + krow * ROWB + (ch << 4)));
 #pragma unroll
-                for (int rb = 0; rb < MB; ++rb)
-                    oacc[db][rb] = mfma16x16x32(a, pb[rb], oacc[db][rb]);
+                    for (int qb = 0; qb < NQB; ++qb) {
+                        if (ks & 1)
+                            sc2[qb] = mfma32x32x16(a, qreg[qb][ks], sc2[qb]);
+                        else
+                            sc[qb] = mfma32x32x16(a, qreg[qb][ks], sc[qb]);
+                    }
+                }
             }
-        }
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb)
+                sc[qb] += sc2[qb];
 
-        // ---- next tile: registers -> LDS, then the loads two tiles ahead ----
-        if (t + 1 < nt) {
-            store_tile(buf ^ 1);
-            load_data();
-            load_idx(t + 3);
+            // ---- softmax: lane holds 16 of the row's 32 tokens, lane^32 the rest ----
+            uint32_t pk[NQB][8];
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb) {
+                if constexpr (decltype(masked)::value) {
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int tok = tok0 + 8 * (v >> 2) + 4 * half + (v & 3);
+                        sc[qb][v] = tok < len ? sc[qb][v] : -INFINITY;
+                    }
+                }
+                float mx = sc[qb][0];
+#pragma unroll
+                for (int v = 1; v < 16; ++v)
+                    mx = fmaxf(mx, sc[qb][v]);
+                mx = fmaxf(mx, swap_halves(mx)) * qk_scale;  // row max, log2 units
+                const bool grow = mx > m_ref[qb] + kRescale;
+                if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+                    // raise the reference of this block (all lanes of the wave)
+                    const float mn = fmaxf(m_ref[qb], mx);
+                    const float alpha = __builtin_amdgcn_exp2f(m_ref[qb] - mn);
+                    m_ref[qb] = mn;
+                    l_part[qb] *= alpha;
+#pragma unroll
+                    for (int db = 0; db < DBW; ++db)
+                        oacc[db][qb] *= alpha;
+                }
+                const float mneg = -m_ref[qb];
+                float rs = 0.0f;
+#pragma unroll
+                for (int v = 0; v < 16; v += 2) {
+                    const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[qb][v], qk_scale, mneg));
+                    const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[qb][v + 1], qk_scale, mneg));
+                    rs += e0 + e1;
+                    pk[qb][v >> 1] = pack_bf16x2(e0, e1);
+                }
+                l_part[qb] += rs;
+            }
+
+            // ---- O^T[dv][query row] += V^T P^T over this wave's columns ----
+            if (pv_wave) {
+#pragma unroll
+                for (int db = 0; db < DBW; ++db) {
+                    const int cb = wave * DWV + db * 32;  // first column of the block
+#pragma unroll
+                    for (int kh = 0; kh < 2; ++kh) {      // 16 tokens per value k-step
+                        u32x4_t a;
+                        if constexpr (FP8) {
+                            const int dv = cb + l32;
+                            uint32_t w4[4];
+#pragma unroll
+                            for (int i2 = 0; i2 < 4; ++i2) {
+                                uint32_t pair = 0;
+#pragma unroll
+                                for (int hh = 0; hh < 2; ++hh) {
+                                    const int s = 2 * i2 + hh;
+                                    const int tok = sub * 32 + kh * 16 + 8 * (s >> 2) + 4 * half + (s & 3);
+                                    const int pc = (dv >> 4) ^ ((tok >> 2) & 3);
+                                    pair |= e4m3_to_bf16(V[tok * ROWB + (pc << 4) + (dv & 15)]) << (16 * hh);
+                                }
+                                w4[i2] = pair;
+                            }
+                            a = u32x4_t{w4[0], w4[1], w4[2], w4[3]};
+                        } else {
+                            // transposing reads: input lane 4t+u of each 16-lane
+                            // group points at row T(t), columns 4u..4u+3; output
+                            // lane j receives column j of rows T(0..3)
+                            const int g16 = lane & 15;
+                            const int col = cb + 16 * ((lane >> 4) & 1) + 4 * (g16 & 3);
+#pragma unroll
+                            for (int r = 0; r < 2; ++r) {
+                                const int tok = sub * 32 + kh * 16 + 8 * r + 4 * half + (g16 >> 2);
+                                const int pc = (col >> 3) ^ ((tok & VSWZ_ROWS) << 2);
+                                const uint8_t *src = V + tok * ROWB + (pc << 4) + (col & 7) * 2;
+                                const i16x4_t v4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                    (__attribute__((address_space(3))) i16x4_t *)(src));
+                                const u32x2_t w2 = __builtin_bit_cast(u32x2_t, v4);
+                                a[2 * r] = w2[0];
+                                a[2 * r + 1] = w2[1];
+                            }
+                        }
+#pragma unroll
+                        for (int qb = 0; qb < NQB; ++qb) {
+                            const u32x4_t b = {pk[qb][4 * kh], pk[qb][4 * kh + 1], pk[qb][4 * kh + 2],
+                                               pk[qb][4 * kh + 3]};
+                            oacc[db][qb] = mfma32x32x16(as_bf16x8(a), as_bf16x8(b), oacc[db][qb]);
+                        }
+                    }
+                }
+            }
+        };
+#pragma unroll
+        for (int sub = 0; sub < NSUB; ++sub) {
+            const int tok0 = t * TN + sub * 32;
+            if (tok0 >= len)
+                break;  // rest of the last tile is past the range
+            if (tok0 + 32 > len)
+                sub_tile(sub, std::true_type{});
+            else
+                sub_tile(sub, std::false_type{});
         }
-        __syncthreads();
     }
+    wait_vm<0>();  // trailing index copies
 
     // ---- epilogue: normalised, v_scale-multiplied partial and its lse ----
 #pragma unroll
-    for (int rb = 0; rb < MB; ++rb) {
-        const int r = row0 + rb * 16 + col;
+    for (int qb = 0; qb < NQB; ++qb) {
+        const float lrow = l_part[qb] + swap_halves(l_part[qb]);
+        const int r = row0 + qb * 32 + l32;
         if (r < rows) {
-            const float inv = p.v_scale / l_run[rb];
+            if (pv_wave) {
+                const float inv = p.v_scale / lrow;
 #pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const int dv = wave * DW + db * 16 + grp * 4;
-                const f32x4_t o = oacc[db][rb] * inv;
-                *(f32x4_t *)(po + (int64_t)r * D + dv) = o;
+                for (int db = 0; db < DBW; ++db)
+#pragma unroll
+                    for (int g4 = 0; g4 < 4; ++g4) {
+                        const int dv = wave * DWV + db * 32 + 8 * g4 + 4 * half;
+                        const f32x4_t o = {oacc[db][qb][4 * g4] * inv, oacc[db][qb][4 * g4 + 1] * inv,
+                                           oacc[db][qb][4 * g4 + 2] * inv, oacc[db][qb][4 * g4 + 3] * inv};
+                        *(f32x4_t *)(po + (int64_t)r * D + dv) = o;
+                    }
             }
-            if (wave == 0 && grp == 0)
-                pl[r] = (m_run[rb] + log2f(l_run[rb])) * kLn2;
+            if (wave == 0 && half == 0)
+                pl[r] = (m_ref[qb] + __log2f(lrow)) * kLn2;
         }
     }
 }
 
 // ---------------------------------------------------------- combine kernel ---
+// One workgroup per output row (sequence b, KV head, query row r).  The four
+// waves split the prefix ranges (s = wave mod 4) and the draft keys
+// (j = wave mod 4); their partial sums meet in LDS and wave 0 merges them.
 template <int D>
 __global__ __launch_bounds__(kThreads) void combine_kernel(const CombineParams p)
 {
     constexpr int VPL = D / 64;  // elements of D / Dv per lane
+    __shared__ __attribute__((aligned(16))) float s_op[4][D];
+    __shared__ __attribute__((aligned(16))) float s_od[4][D];
+    __shared__ float s_md[4], s_dd[4];
+
     const int lane = threadIdx.x & 63;
-    const int64_t gw = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int64_t total = (int64_t)p.bs * p.h_kv * p.rows;
-    if (gw >= total)
-        return;
-    const int r = (int)(gw % p.rows);
-    const int64_t t = gw / p.rows;
+    const int wave = threadIdx.x >> 6;
+    const int64_t gr = blockIdx.x;
+    const int r = (int)(gr % p.rows);
+    const int64_t t = gr / p.rows;
     const int kvh = (int)(t % p.h_kv);
     const int b = (int)(t / p.h_kv);
     const int hg = r / p.l_ext;
@@ -537,48 +713,55 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const CombineParams p
     const int qo = p.qo_indptr[b];
     const int d0 = lane * VPL;
 
-    // ---- (a) log-sum-exp merge of the prefix ranges ----
+    // ---- (a) prefix ranges: global max / normaliser, then this wave's share ----
     int32_t base, count;
     ranges_of(p.kv_indptr, p.bs, p.mode, p.split_tokens, p.n_splits, b, &base, &count);
+    const float *lse_row = p.part_lse + ((int64_t)base * p.h_kv + kvh) * p.rows + r;
+    const int64_t lse_step = (int64_t)p.h_kv * p.rows;  // next range, same head and row
+    float m = -INFINITY;
+    for (int s = lane; s < count; s += 64)
+        m = fmaxf(m, lse_row[s * lse_step]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        m = fmaxf(m, __shfl_xor(m, off));
+    float den = 0.0f;
     float acc[VPL];
 #pragma unroll
     for (int v = 0; v < VPL; ++v)
         acc[v] = 0.0f;
-    float m = -INFINITY, den = 0.0f;
-    for (int s = 0; s < count; ++s) {
-        const int64_t slot = (int64_t)(base + s) * p.h_kv + kvh;
-        const float lse = p.part_lse[slot * p.rows + r];
-        if (lse == -INFINITY)
-            continue;  // empty range
-        const float *o = p.part_o + (slot * p.rows + r) * D + d0;
-        float ov[VPL];
-        if constexpr (VPL == 4) {
-            const f32x4_t x = *(const f32x4_t *)o;
-            ov[0] = x[0];
-            ov[1] = x[1];
-            ov[2] = x[2];
-            ov[3] = x[3];
-        } else {
+    if (m > -INFINITY) {
+        for (int s = lane; s < count; s += 64)
+            den += expf(lse_row[s * lse_step] - m);
 #pragma unroll
-            for (int v = 0; v < VPL; ++v)
-                ov[v] = o[v];
+        for (int off = 32; off > 0; off >>= 1)
+            den += __shfl_xor(den, off);
+        // weighted sum of this wave's ranges; iterations are independent, so
+        // their loads issue back to back.  An empty range has weight 0, output 0.
+        const float *o_row = p.part_o + (((int64_t)base * p.h_kv + kvh) * p.rows + r) * D + d0;
+        const int64_t o_step = lse_step * D;
+#pragma unroll 4
+        for (int s = wave; s < count; s += 4) {
+            const float w = expf(lse_row[s * lse_step] - m);
+            const float *o = o_row + s * o_step;
+            if constexpr (VPL == 4) {
+                const f32x4_t x = *(const f32x4_t *)o;
+                acc[0] += w * x[0];
+                acc[1] += w * x[1];
+                acc[2] += w * x[2];
+                acc[3] += w * x[3];
+            } else {
+#pragma unroll
+                for (int v = 0; v < VPL; ++v)
+                    acc[v] += w * o[v];
+            }
         }
-        const float mn = fmaxf(m, lse);
-        const float a = expf(m - mn);
-        const float w = expf(lse - mn);
-#pragma unroll
-        for (int v = 0; v < VPL; ++v)
-            acc[v] = acc[v] * a + w * ov[v];
-        den = den * a + w;
-        m = mn;
     }
-    float op[VPL];
-    const float lse_p = den > 0.0f ? m + logf(den) : -INFINITY;
 #pragma unroll
     for (int v = 0; v < VPL; ++v)
-        op[v] = den > 0.0f ? acc[v] / den : 0.0f;
+        s_op[wave][d0 + v] = acc[v];
 
-    // ---- (b) causal draft block: keys j <= di, fp32, no cast, no scales ----
+    // ---- (b) causal draft keys j <= di, this wave's j = wave mod 4 ----
+    // fp32, query not cast, no k/v scale
     float qv[VPL];
     {
         const uint16_t *qr = p.q + (int64_t)(qo + di) * p.q_s0 + (int64_t)h * p.q_s1 + d0;
@@ -591,7 +774,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const CombineParams p
     for (int v = 0; v < VPL; ++v)
         od[v] = 0.0f;
     float md = -INFINITY, dd = 0.0f;
-    for (int j = 0; j <= di; ++j) {
+    for (int j = wave; j <= di; j += 4) {
         const uint16_t *kr = p.k_ext + (int64_t)(qo + j) * p.ke_s0 + (int64_t)kvh * p.ke_s1 + d0;
         const uint16_t *vr = p.v_ext + (int64_t)(qo + j) * p.ve_s0 + (int64_t)kvh * p.ve_s1 + d0;
         float dot = 0.0f;
@@ -601,57 +784,86 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const CombineParams p
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1)
             dot += __shfl_xor(dot, off);
-        const float s = dot * p.sm_scale;
-        const float mn = fmaxf(md, s);
+        const float sj = dot * p.sm_scale;
+        const float mn = fmaxf(md, sj);
         const float a = expf(md - mn);
-        const float w = expf(s - mn);
+        const float w = expf(sj - mn);
 #pragma unroll
         for (int v = 0; v < VPL; ++v)
             od[v] = od[v] * a + w * bf16_to_f32(vr[v]);
         dd = dd * a + w;
         md = mn;
     }
-    const float lse_d = md + logf(dd);
+#pragma unroll
+    for (int v = 0; v < VPL; ++v)
+        s_od[wave][d0 + v] = od[v];
+    if (lane == 0) {
+        s_md[wave] = md;
+        s_dd[wave] = dd;
+    }
+    __syncthreads();
+    if (wave != 0)
+        return;
 
-    // ---- (c) final merge of prefix and draft, bf16 store ----
+    // ---- (c) merge the waves' shares; final prefix / draft merge; bf16 store ----
+    float mdx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+        mdx = fmaxf(mdx, s_md[w]);
+    float sw[4], ddx = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        sw[w] = s_md[w] == -INFINITY ? 0.0f : expf(s_md[w] - mdx);
+        ddx += sw[w] * s_dd[w];
+    }
+    const float lse_d = mdx + logf(ddx);
+    const float lse_p = den > 0.0f ? m + logf(den) : -INFINITY;
     const float mm = fmaxf(lse_p, lse_d);
     const float wp = expf(lse_p - mm);
     const float wd = expf(lse_d - mm);
     const float inv = 1.0f / (wp + wd);
+    const float cp = den > 0.0f ? wp / den : 0.0f;  // prefix partial sums -> output
+    const float cd = wd / ddx;                      // draft partial sums -> output
     uint16_t *orow = p.out + (int64_t)(qo + di) * p.o_s0 + (int64_t)h * p.o_s1 + d0;
 #pragma unroll
-    for (int v = 0; v < VPL; ++v)
-        orow[v] = (uint16_t)f32_to_bf16_rne((op[v] * wp + (od[v] / dd) * wd) * inv);
+    for (int v = 0; v < VPL; ++v) {
+        float sp = 0.0f, sd = 0.0f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            sp += s_op[w][d0 + v];
+            sd += sw[w] * s_od[w][d0 + v];
+        }
+        orow[v] = (uint16_t)f32_to_bf16_rne((sp * cp + sd * cd) * inv);
+    }
 }
 
 // ----------------------------------------------------------------- launch ---
 template <bool FP8, int D>
-static int launch_prefix_mb(const PrefixParams &p, int mb, int64_t blocks, hipStream_t s)
+static int launch_prefix_qb(const PrefixParams &p, int qblocks, int64_t blocks, hipStream_t s)
 {
     dim3 grid((unsigned)blocks), block(kThreads);
-    switch (mb) {
-    case 1: hipLaunchKernelGGL((prefix_kernel<FP8, D, 1>), grid, block, 0, s, p); break;
-    case 2: hipLaunchKernelGGL((prefix_kernel<FP8, D, 2>), grid, block, 0, s, p); break;
-    default: hipLaunchKernelGGL((prefix_kernel<FP8, D, 4>), grid, block, 0, s, p); break;
-    }
+    if (qblocks == 1)
+        hipLaunchKernelGGL((prefix_kernel<FP8, D, 1>), grid, block, 0, s, p);
+    else
+        hipLaunchKernelGGL((prefix_kernel<FP8, D, 2>), grid, block, 0, s, p);
     return (int)hipGetLastError();
 }
 
-int launch_prefix(const PrefixParams &p, int head_dim, bool kv_fp8, int row_blocks, int64_t blocks,
+int launch_prefix(const PrefixParams &p, int head_dim, bool kv_fp8, int qblocks, int64_t blocks,
                   void *stream)
 {
     hipStream_t s = (hipStream_t)stream;
     if (kv_fp8) {
         switch (head_dim) {
-        case 64: return launch_prefix_mb<true, 64>(p, row_blocks, blocks, s);
-        case 128: return launch_prefix_mb<true, 128>(p, row_blocks, blocks, s);
-        default: return launch_prefix_mb<true, 256>(p, row_blocks, blocks, s);
+        case 64: return launch_prefix_qb<true, 64>(p, qblocks, blocks, s);
+        case 128: return launch_prefix_qb<true, 128>(p, qblocks, blocks, s);
+        default: return launch_prefix_qb<true, 256>(p, qblocks, blocks, s);
         }
     }
     switch (head_dim) {
-    case 64: return launch_prefix_mb<false, 64>(p, row_blocks, blocks, s);
-    case 128: return launch_prefix_mb<false, 128>(p, row_blocks, blocks, s);
-    default: return launch_prefix_mb<false, 256>(p, row_blocks, blocks, s);
+    case 64: return launch_prefix_qb<false, 64>(p, qblocks, blocks, s);
+    case 128: return launch_prefix_qb<false, 128>(p, qblocks, blocks, s);
+    default: return launch_prefix_qb<false, 256>(p, qblocks, blocks, s);
     }
 }
 

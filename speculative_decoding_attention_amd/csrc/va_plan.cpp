@@ -88,6 +88,8 @@ int check_desc(const va_desc_t *d, int32_t l_ext)
         !aligned_strides(d->vext_stride, 2) || !aligned_strides(d->out_stride, 2) ||
         !aligned_strides(d->kbuf_stride, kv_bytes) || !aligned_strides(d->vbuf_stride, kv_bytes))
         return fail(VA_ERR_STRIDE, "every row and head stride must be a multiple of 16 bytes");
+    if (d->kbuf_stride[0] * kv_bytes > (int64_t)UINT32_MAX || d->vbuf_stride[0] * kv_bytes > (int64_t)UINT32_MAX)
+        return fail(VA_ERR_STRIDE, "pool row stride above 4 GiB");
     // The output is written: its rows must not overlap.
     if (d->out_stride[1] < d->v_head_dim || d->out_stride[0] < (int64_t)d->h_q * d->out_stride[1])
         return fail(VA_ERR_STRIDE, "out strides (%lld, %lld) make output rows overlap",
@@ -147,7 +149,7 @@ int make_plan(const va_desc_t *d, int32_t l_ext, int32_t num_cus, va_plan_t *pla
         return fail(VA_ERR_SIZE, "rows per KV head (%lld) too large", (long long)rows);
     p.rows = (int32_t)rows;
     p.row_chunks = (int32_t)((rows + kRowChunk - 1) / kRowChunk);
-    p.tile_tokens = tile_tokens_for(d->head_dim);
+    p.tile_tokens = tile_tokens_for(d->head_dim, d->kv_dtype == VA_DTYPE_FP8_E4M3FN ? 1 : 2);
     const int64_t T = d->num_kv_indices;
     if (d->n_splits > 0) {
         p.mode = 1;
@@ -172,7 +174,7 @@ int make_plan(const va_desc_t *d, int32_t l_ext, int32_t num_cus, va_plan_t *pla
     }
     const int64_t slots = p.range_slots * d->h_kv;
     p.prefix_blocks = slots * p.row_chunks;
-    p.combine_blocks = ((int64_t)d->bs * d->h_kv * rows + 3) / 4;
+    p.combine_blocks = (int64_t)d->bs * d->h_kv * rows;  // one workgroup per output row
     if (p.prefix_blocks > INT32_MAX || p.combine_blocks > INT32_MAX || p.range_slots > INT32_MAX)
         return fail(VA_ERR_SIZE, "grid too large (%lld prefix workgroups)", (long long)p.prefix_blocks);
     const int64_t o_bytes = align_up(slots * rows * d->v_head_dim * 4, 256);

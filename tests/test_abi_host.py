@@ -100,7 +100,7 @@ def _plan_for(p: W.Problem, cus=256, **kw):
 
 def test_plan_headline_shapes():
     # B=8, 8k prefix, l_ext=4, 16/2 heads, D=256: 2 KV heads x 65536 tokens
-    # shared over 2 resident workgroups per CU on 256 CUs -> 256-token ranges
+    # shared over two resident workgroups per CU on 256 CUs -> 256-token ranges
     meta = meta_problem(bs=8, n=8192)
     plan = va.verify_attn_plan(va.make_desc(**meta), 4, 256)
     assert plan.mode == 0 and plan.split_tokens == 256
