@@ -14,13 +14,16 @@ namespace va {
 constexpr int kRowChunk = 64;
 // Granule of the pages' equal-split rule (ranges are rounded up to it).
 constexpr int kEvenSplitGranule = 32;
-// Threads per workgroup of both kernels (4 wavefronts of 64).
+// Threads per workgroup of the combine kernel (4 wavefronts of 64).
 constexpr int kThreads = 256;
-// Depth of the prefix kernel's LDS ring of K/V tiles (<= 32 KB per tile) and
-// the workgroups per CU that leaves room for in 160 KB of LDS; the split
-// heuristic aims for that many resident workgroups per CU.
-constexpr int kRingStages = 2;
-constexpr int kResidentPerCU = kRingStages == 2 ? 2 : 1;
+// Prefix kernel shape.  A workgroup is one group of 4 waves per 32-row query
+// block.  One query block: 4 waves and a 2-tile LDS ring of K/V tiles
+// (<= 32 KB each), two workgroups per CU (their tiles differ, so no score work
+// is repeated).  Two query blocks: 8 waves and a 4-tile ring, one workgroup
+// per CU.  The split heuristic aims for that many resident workgroups per CU.
+constexpr int prefix_waves(int qblocks) { return qblocks == 1 ? 4 : 8; }
+constexpr int prefix_ring_stages(int qblocks) { return qblocks == 1 ? 2 : 4; }
+constexpr int prefix_resident_per_cu(int qblocks) { return qblocks == 1 ? 2 : 1; }
 // Smallest range the heuristic chooses; ranges are multiples of this.
 constexpr int kSplitQuantum = 64;
 

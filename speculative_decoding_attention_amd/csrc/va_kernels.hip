@@ -96,29 +96,35 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t 
 // ceil(ceil(n_b / n_splits) / 32) * 32 tokens, empty past the end.
 struct Range {
     int32_t b;
-    int32_t start;
+    int32_t start;    // token range [start, end) of sequence b's prefix
     int32_t end;
+    int32_t kv_base;  // kv_indptr[b]
+    int32_t qo;       // qo_indptr[b]
     bool valid;
 };
 
-// Number of mode-0 ranges of sequences [0, b_end), and the whole-wave lookup
-// of the sequence that owns range `target` (both use the same wave scan).
-__device__ __forceinline__ Range locate_range(const int32_t *kv_indptr, int32_t bs, int32_t mode,
-                                              int32_t split_tokens, int32_t n_splits,
-                                              int64_t cidx)
+// Whole-wave lookup of range `cidx`: the sequence that owns it, its token
+// range, and that sequence's kv_indptr / qo_indptr entries (read by the same
+// loads as the scan, so no second round trip).
+__device__ __forceinline__ Range locate_range(const int32_t *kv_indptr, const int32_t *qo_indptr,
+                                              int32_t bs, int32_t mode, int32_t split_tokens,
+                                              int32_t n_splits, int64_t cidx)
 {
-    Range r = {0, 0, 0, false};
+    Range r = {0, 0, 0, 0, 0, false};
     if (mode == 1) {
         const int64_t b = cidx / n_splits;
         if (b >= bs)
             return r;
         const int32_t s = (int32_t)(cidx % n_splits);
-        const int32_t n = kv_indptr[b + 1] - kv_indptr[b];
+        const int32_t k0 = kv_indptr[b];
+        const int32_t n = kv_indptr[b + 1] - k0;
         const int32_t per = ((n + n_splits - 1) / n_splits + kEvenSplitGranule - 1) /
                             kEvenSplitGranule * kEvenSplitGranule;
         r.b = (int32_t)b;
         r.start = s * per;
         r.end = min(r.start + per, n);
+        r.kv_base = k0;
+        r.qo = qo_indptr[b];
         r.valid = true;
         return r;
     }
@@ -126,7 +132,9 @@ __device__ __forceinline__ Range locate_range(const int32_t *kv_indptr, int32_t 
     int64_t cum = 0;
     for (int32_t b0 = 0; b0 < bs; b0 += 64) {
         const int32_t b = b0 + lane;
-        const int32_t n = b < bs ? kv_indptr[b + 1] - kv_indptr[b] : 0;
+        const int32_t k0 = b < bs ? kv_indptr[b] : 0;
+        const int32_t n = b < bs ? kv_indptr[b + 1] - k0 : 0;
+        const int32_t q0 = b < bs ? qo_indptr[b] : 0;
         const int32_t nch = (n + split_tokens - 1) / split_tokens;
         int32_t incl = nch;
 #pragma unroll
@@ -145,6 +153,8 @@ __device__ __forceinline__ Range locate_range(const int32_t *kv_indptr, int32_t 
             r.b = b0 + first;
             r.start = c * split_tokens;
             r.end = min(r.start + split_tokens, nf);
+            r.kv_base = __shfl(k0, first);
+            r.qo = __shfl(q0, first);
             r.valid = true;
             return r;
         }
@@ -222,21 +232,22 @@ __device__ __forceinline__ u32x4_t fp8x8_to_bf16(u32x2_t v)
     return o;
 }
 
-template <bool FP8, int D>
+template <bool FP8, int D, int NQB>
 struct PrefixGeom {
+    static constexpr int NW = prefix_waves(NQB);
     static constexpr int E = FP8 ? 1 : 2;               // pool bytes per element
     static constexpr int ROWB = D * E;                  // pool bytes per K (or V) row
     static constexpr int TN0 = 16384 / ROWB;
     static constexpr int TN = TN0 > 128 ? 128 : TN0;    // tokens per tile (K+V <= 32 KB)
     static constexpr int LCH = ROWB / 16;               // 16-byte chunks per row
     static constexpr int RPI = 64 / LCH;                // rows per wave-wide copy
-    static constexpr int NBUF = kRingStages;            // tiles in the LDS ring
+    static constexpr int NBUF = prefix_ring_stages(NQB);  // tiles in the LDS ring
     static constexpr int STAGE_K = TN * ROWB;
     static constexpr int STAGE = 2 * STAGE_K;           // K tile then V tile
-    static constexpr int NIKW = TN * LCH / 256;         // K copies per wave per tile (V: same)
+    static constexpr int NIKW = TN * LCH / (64 * NW);   // K copies per wave per tile (V: same)
     static constexpr int RW = NIKW * RPI;               // rows each wave copies per tile
     static constexpr int NIDX = 3;                      // index slots per wave
-    static_assert(NIKW >= 1 && NIKW * 256 == TN * LCH, "tile / copy geometry");
+    static_assert(NIKW >= 1 && NIKW * 64 * NW == TN * LCH, "tile / copy geometry");
     static_assert(2 * RW <= 64, "one index copy per wave per tile");
     static_assert(TN == tile_tokens_for(D, E), "host and kernel tile rules agree");
 };
@@ -300,9 +311,10 @@ __device__ __forceinline__ uint32_t e4m3_code(float v)
 }
 
 template <bool FP8, int D, int NQB>
-__global__ __launch_bounds__(kThreads) void prefix_kernel(const PrefixParams p)
+__global__ __launch_bounds__(prefix_waves(NQB) * 64) void prefix_kernel(const PrefixParams p)
 {
-    using G = PrefixGeom<FP8, D>;
+    using G = PrefixGeom<FP8, D, NQB>;
+    constexpr int NW = G::NW;
     constexpr int TN = G::TN;
     constexpr int ROWB = G::ROWB;
     constexpr int LCH = G::LCH;
@@ -311,7 +323,8 @@ __global__ __launch_bounds__(kThreads) void prefix_kernel(const PrefixParams p)
     constexpr int RW = G::RW;
     constexpr int NKS = D / 16;             // k-steps of the score MFMA
     constexpr int NSUB = TN / 32;           // 32-token sub-tiles per tile
-    constexpr int NPVW = D >= 128 ? 4 : D / 32;  // waves that own output columns
+    constexpr int GW = NW / NQB;            // waves per query block
+    constexpr int NPVW = GW < D / 32 ? GW : D / 32;  // waves of a block that own output columns
     constexpr int DWV = D / NPVW;           // output columns per such wave
     constexpr int DBW = DWV / 32;           // 32-column blocks per such wave
     constexpr int KSWZ = (LCH < 16 ? LCH : 16) - 1;
@@ -327,7 +340,7 @@ __global__ __launch_bounds__(kThreads) void prefix_kernel(const PrefixParams p)
     constexpr int VM_NONE_AHEAD = 2;
 
     __shared__ __attribute__((aligned(1024))) uint8_t s_ring[NBUF * G::STAGE];
-    __shared__ __attribute__((aligned(16))) int64_t s_idx[4][G::NIDX][RW];
+    __shared__ __attribute__((aligned(16))) int64_t s_idx[NW][G::NIDX][RW];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -341,7 +354,7 @@ __global__ __launch_bounds__(kThreads) void prefix_kernel(const PrefixParams p)
     const int64_t t1 = blk / p.row_chunks;
     const int kvh = (int)(t1 % p.h_kv);
     const int64_t cidx = t1 / p.h_kv;
-    const Range rg = locate_range(p.kv_indptr, p.bs, p.mode, p.split_tokens, p.n_splits, cidx);
+    const Range rg = locate_range(p.kv_indptr, p.qo_indptr, p.bs, p.mode, p.split_tokens, p.n_splits, cidx);
     if (!rg.valid)
         return;  // surplus slot of the static grid: never read by the combine pass
     const int64_t slot = cidx * p.h_kv + kvh;
@@ -354,24 +367,24 @@ __global__ __launch_bounds__(kThreads) void prefix_kernel(const PrefixParams p)
         // Empty range: output 0 and log-sum-exp -inf, so the merge weight is
         // exactly 0 and no stale value can leak in.
         const int nr = min(rows - row0, NQB * 32);
-        for (int e = tid; e < nr * D; e += kThreads)
+        for (int e = tid; e < nr * D; e += NW * 64)
             po[(int64_t)(row0 + e / D) * D + (e % D)] = 0.0f;
         if (tid < nr)
             pl[row0 + tid] = -INFINITY;
         return;
     }
 
-    const int64_t kv0 = (int64_t)p.kv_indptr[rg.b] + rg.start;
+    const int64_t kv0 = (int64_t)rg.kv_base + rg.start;
     const int len = rg.end - rg.start;
     const int nt = (len + TN - 1) / TN;
-    const int qo = p.qo_indptr[rg.b];
+    const int qo = rg.qo;
     const uint32_t ring = lds_offset(s_ring);
 
     // ---- query tile -> ring stage NBUF-1 (bf16 rows of D, row-major) ----
     {
         constexpr int QCH = D / 8;                    // 16-byte chunks per query row
         constexpr int QI = NQB * 32 * QCH / 64;       // wave-wide copies for the tile
-        for (int i = wave; i < QI; i += 4) {
+        for (int i = wave; i < QI; i += NW) {
             const int e = i * 64 + lane;
             const int r = row0 + e / QCH;             // query row of this chunk
             const int rr = r < rows ? r : row0;       // padding rows copy a valid row
@@ -447,12 +460,15 @@ __global__ __launch_bounds__(kThreads) void prefix_kernel(const PrefixParams p)
     }
     lds_barrier();
 
+    // ---- this wave's query block (waves qbw*GW .. +GW share it) ----
+    const int qbw = wave / GW;   // query block of this wave
+    const int wg = wave % GW;    // wave within the block's group
+
     // ---- query operand (B: col = query row, k = d): bf16 or E4M3FN codes ----
     typedef typename std::conditional<FP8, uint64_t, bf16x8_t>::type qop_t;
-    qop_t qreg[NQB][NKS];
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-        const int rl = qb * 32 + l32;
+    qop_t qreg[NKS];
+    {
+        const int rl = qbw * 32 + l32;
         const bool rv = row0 + rl < rows;
         const uint8_t *qrow = s_ring + (NBUF - 1) * G::STAGE + (rv ? rl : 0) * D * 2;
 #pragma unroll
@@ -468,25 +484,20 @@ __global__ __launch_bounds__(kThreads) void prefix_kernel(const PrefixParams p)
                     const uint32_t h = (raw[e >> 1] >> (16 * (e & 1))) & 0xffffu;
                     codes |= (uint64_t)e4m3_code(round_to_e4m3(bf16_to_f32(h))) << (8 * e);
                 }
-                qreg[qb][ks] = codes;
+                qreg[ks] = codes;
             } else {
-                qreg[qb][ks] = as_bf16x8(raw);
+                qreg[ks] = as_bf16x8(raw);
             }
         }
     }
 
-    // ---- running state: lane's query row in block qb is 32*qb + l32 ----
-    float m_ref[NQB], l_part[NQB];
-    f32x16_t oacc[DBW][NQB];
+    // ---- running state: lane's query row is 32*qbw + l32 ----
+    float m_ref = -INFINITY, l_part = 0.0f;
+    f32x16_t oacc[DBW];
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-        m_ref[qb] = -INFINITY;
-        l_part[qb] = 0.0f;
-#pragma unroll
-        for (int db = 0; db < DBW; ++db)
-            oacc[db][qb] = f32x16_t{};
-    }
-    const bool pv_wave = wave < NPVW;
+    for (int db = 0; db < DBW; ++db)
+        oacc[db] = f32x16_t{};
+    const bool pv_wave = wg < NPVW;
 
     const float qk_scale = p.qk_scale_log2;
     for (int t = 0; t < nt; ++t) {
@@ -522,90 +533,74 @@ __global__ __launch_bounds__(kThreads) void prefix_kernel(const PrefixParams p)
         auto sub_tile = [&](const int sub, auto masked) {
             const int tok0 = t * TN + sub * 32;  // first token of the sub-tile
 
-            // ---- scores S^T[token][query row], 32 x 32 per query block ----
-            // two accumulators per block (even / odd k-steps) halve the chain of
-            // dependent MFMAs
-            f32x16_t sc[NQB], sc2[NQB];
-#pragma unroll
-            for (int qb = 0; qb < NQB; ++qb) {
-                sc[qb] = f32x16_t{};
-                sc2[qb] = f32x16_t{};
-            }
+            // ---- scores S^T[token][query row] of this wave's block, 32 x 32 ----
+            // two accumulators (even / odd k-steps) halve the chain of dependent
+            // MFMAs
+            f32x16_t sc = {}, sc2 = {};
             const int krow = sub * 32 + l32;
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
                 if constexpr (FP8) {
                     const int ch = ks ^ (krow & KSWZ);
                     const uint64_t a = *(const uint64_t *)(K + krow * ROWB + (ch << 4) + half * 8);
-#pragma unroll
-                    for (int qb = 0; qb < NQB; ++qb) {
-                        if (ks & 1)
-                            sc2[qb] = mfma32x32x16_fp8(a, qreg[qb][ks], sc2[qb]);
-                        else
-                            sc[qb] = mfma32x32x16_fp8(a, qreg[qb][ks], sc[qb]);
-                    }
+                    if (ks & 1)
+                        sc2 = mfma32x32x16_fp8(a, qreg[ks], sc2);
+                    else
+                        sc = mfma32x32x16_fp8(a, qreg[ks], sc);
                 } else {
                     const int ch = (ks * 2 + half) ^ (krow & KSWZ);
                     const bf16x8_t a = as_bf16x8(*(const u32x4_t *)(K + krow * ROWB + (ch << 4)));
-#pragma unroll
-                    for (int qb = 0; qb < NQB; ++qb) {
-                        if (ks & 1)
-                            sc2[qb] = mfma32x32x16(a, qreg[qb][ks], sc2[qb]);
-                        else
-                            sc[qb] = mfma32x32x16(a, qreg[qb][ks], sc[qb]);
-                    }
+                    if (ks & 1)
+                        sc2 = mfma32x32x16(a, qreg[ks], sc2);
+                    else
+                        sc = mfma32x32x16(a, qreg[ks], sc);
                 }
             }
-#pragma unroll
-            for (int qb = 0; qb < NQB; ++qb)
-                sc[qb] += sc2[qb];
+            sc += sc2;
 
             // ---- softmax: lane holds 16 of the row's 32 tokens, lane^32 the rest ----
-            uint32_t pk[NQB][8];
+            if constexpr (decltype(masked)::value) {
 #pragma unroll
-            for (int qb = 0; qb < NQB; ++qb) {
-                if constexpr (decltype(masked)::value) {
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int tok = tok0 + 8 * (v >> 2) + 4 * half + (v & 3);
-                        sc[qb][v] = tok < len ? sc[qb][v] : -INFINITY;
-                    }
+                for (int v = 0; v < 16; ++v) {
+                    const int tok = tok0 + 8 * (v >> 2) + 4 * half + (v & 3);
+                    sc[v] = tok < len ? sc[v] : -INFINITY;
                 }
-                float mx = sc[qb][0];
-#pragma unroll
-                for (int v = 1; v < 16; ++v)
-                    mx = fmaxf(mx, sc[qb][v]);
-                mx = fmaxf(mx, swap_halves(mx)) * qk_scale;  // row max, log2 units
-                const bool grow = mx > m_ref[qb] + kRescale;
-                if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-                    // raise the reference of this block (all lanes of the wave)
-                    const float mn = fmaxf(m_ref[qb], mx);
-                    const float alpha = __builtin_amdgcn_exp2f(m_ref[qb] - mn);
-                    m_ref[qb] = mn;
-                    l_part[qb] *= alpha;
-#pragma unroll
-                    for (int db = 0; db < DBW; ++db)
-                        oacc[db][qb] *= alpha;
-                }
-                const float mneg = -m_ref[qb];
-                float rs = 0.0f;
-#pragma unroll
-                for (int v = 0; v < 16; v += 2) {
-                    const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[qb][v], qk_scale, mneg));
-                    const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[qb][v + 1], qk_scale, mneg));
-                    rs += e0 + e1;
-                    pk[qb][v >> 1] = pack_bf16x2(e0, e1);
-                }
-                l_part[qb] += rs;
             }
+            float mx = sc[0];
+#pragma unroll
+            for (int v = 1; v < 16; ++v)
+                mx = fmaxf(mx, sc[v]);
+            mx = fmaxf(mx, swap_halves(mx)) * qk_scale;  // row max, log2 units
+            const bool grow = mx > m_ref + kRescale;
+            if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+                // raise the reference (all lanes of the wave)
+                const float mn = fmaxf(m_ref, mx);
+                const float alpha = __builtin_amdgcn_exp2f(m_ref - mn);
+                m_ref = mn;
+                l_part *= alpha;
+#pragma unroll
+                for (int db = 0; db < DBW; ++db)
+                    oacc[db] *= alpha;
+            }
+            const float mneg = -m_ref;
+            float rs = 0.0f;
+            uint32_t pk[8];
+#pragma unroll
+            for (int v = 0; v < 16; v += 2) {
+                const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[v], qk_scale, mneg));
+                const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[v + 1], qk_scale, mneg));
+                rs += e0 + e1;
+                pk[v >> 1] = pack_bf16x2(e0, e1);
+            }
+            l_part += rs;
 
             // ---- O^T[dv][query row] += V^T P^T over this wave's columns ----
             if (pv_wave) {
 #pragma unroll
                 for (int db = 0; db < DBW; ++db) {
-                    const int cb = wave * DWV + db * 32;  // first column of the block
+                    const int cb = wg * DWV + db * 32;  // first column of the block
 #pragma unroll
-                    for (int kh = 0; kh < 2; ++kh) {      // 16 tokens per value k-step
+                    for (int kh = 0; kh < 2; ++kh) {    // 16 tokens per value k-step
                         u32x4_t a;
                         if constexpr (FP8) {
                             const int dv = cb + l32;
@@ -641,12 +636,8 @@ __global__ __launch_bounds__(kThreads) void prefix_kernel(const PrefixParams p)
                                 a[2 * r + 1] = w2[1];
                             }
                         }
-#pragma unroll
-                        for (int qb = 0; qb < NQB; ++qb) {
-                            const u32x4_t b = {pk[qb][4 * kh], pk[qb][4 * kh + 1], pk[qb][4 * kh + 2],
-                                               pk[qb][4 * kh + 3]};
-                            oacc[db][qb] = mfma32x32x16(as_bf16x8(a), as_bf16x8(b), oacc[db][qb]);
-                        }
+                        const u32x4_t bop = {pk[4 * kh], pk[4 * kh + 1], pk[4 * kh + 2], pk[4 * kh + 3]};
+                        oacc[db] = mfma32x32x16(as_bf16x8(a), as_bf16x8(bop), oacc[db]);
                     }
                 }
             }
@@ -665,10 +656,9 @@ __global__ __launch_bounds__(kThreads) void prefix_kernel(const PrefixParams p)
     wait_vm<0>();  // trailing index copies
 
     // ---- epilogue: normalised, v_scale-multiplied partial and its lse ----
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-        const float lrow = l_part[qb] + swap_halves(l_part[qb]);
-        const int r = row0 + qb * 32 + l32;
+    {
+        const float lrow = l_part + swap_halves(l_part);
+        const int r = row0 + qbw * 32 + l32;
         if (r < rows) {
             if (pv_wave) {
                 const float inv = p.v_scale / lrow;
@@ -676,14 +666,14 @@ __global__ __launch_bounds__(kThreads) void prefix_kernel(const PrefixParams p)
                 for (int db = 0; db < DBW; ++db)
 #pragma unroll
                     for (int g4 = 0; g4 < 4; ++g4) {
-                        const int dv = wave * DWV + db * 32 + 8 * g4 + 4 * half;
-                        const f32x4_t o = {oacc[db][qb][4 * g4] * inv, oacc[db][qb][4 * g4 + 1] * inv,
-                                           oacc[db][qb][4 * g4 + 2] * inv, oacc[db][qb][4 * g4 + 3] * inv};
+                        const int dv = wg * DWV + db * 32 + 8 * g4 + 4 * half;
+                        const f32x4_t o = {oacc[db][4 * g4] * inv, oacc[db][4 * g4 + 1] * inv,
+                                           oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv};
                         *(f32x4_t *)(po + (int64_t)r * D + dv) = o;
                     }
             }
-            if (wave == 0 && half == 0)
-                pl[r] = (m_ref[qb] + __log2f(lrow)) * kLn2;
+            if (wg == 0 && half == 0)
+                pl[r] = (m_ref + __log2f(lrow)) * kLn2;
         }
     }
 }
@@ -692,10 +682,13 @@ __global__ __launch_bounds__(kThreads) void prefix_kernel(const PrefixParams p)
 // One workgroup per output row (sequence b, KV head, query row r).  The four
 // waves split the prefix ranges (s = wave mod 4) and the draft keys
 // (j = wave mod 4); their partial sums meet in LDS and wave 0 merges them.
+// Loads are issued in two dependent rounds only: the index pointers, then
+// every log-sum-exp, this wave's partial outputs and its draft rows at once.
 template <int D>
 __global__ __launch_bounds__(kThreads) void combine_kernel(const CombineParams p)
 {
     constexpr int VPL = D / 64;  // elements of D / Dv per lane
+    constexpr int PRE = 8;       // partial outputs per wave loaded up front
     __shared__ __attribute__((aligned(16))) float s_op[4][D];
     __shared__ __attribute__((aligned(16))) float s_od[4][D];
     __shared__ float s_md[4], s_dd[4];
@@ -710,17 +703,67 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const CombineParams p
     const int hg = r / p.l_ext;
     const int di = r % p.l_ext;
     const int h = kvh * p.group + hg;
-    const int qo = p.qo_indptr[b];
     const int d0 = lane * VPL;
 
-    // ---- (a) prefix ranges: global max / normaliser, then this wave's share ----
+    // ---- round 1: where this sequence's rows and ranges are ----
+    const int qo = p.qo_indptr[b];
     int32_t base, count;
     ranges_of(p.kv_indptr, p.bs, p.mode, p.split_tokens, p.n_splits, b, &base, &count);
+
+    // ---- round 2: everything else ----
     const float *lse_row = p.part_lse + ((int64_t)base * p.h_kv + kvh) * p.rows + r;
     const int64_t lse_step = (int64_t)p.h_kv * p.rows;  // next range, same head and row
+    const float *o_row = p.part_o + (((int64_t)base * p.h_kv + kvh) * p.rows + r) * D + d0;
+    const int64_t o_step = lse_step * D;
+    float ov[PRE][VPL], lw[PRE];
+#pragma unroll
+    for (int i = 0; i < PRE; ++i) {
+        const int s = wave + 4 * i;
+        lw[i] = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v)
+            ov[i][v] = 0.0f;
+        if (s < count) {
+            lw[i] = lse_row[s * lse_step];
+            const float *o = o_row + s * o_step;
+            if constexpr (VPL == 4) {
+                const f32x4_t x = *(const f32x4_t *)o;
+                ov[i][0] = x[0];
+                ov[i][1] = x[1];
+                ov[i][2] = x[2];
+                ov[i][3] = x[3];
+            } else {
+#pragma unroll
+                for (int v = 0; v < VPL; ++v)
+                    ov[i][v] = o[v];
+            }
+        }
+    }
+    float qv[VPL];
+    {
+        const uint16_t *qr = p.q + (int64_t)(qo + di) * p.q_s0 + (int64_t)h * p.q_s1 + d0;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v)
+            qv[v] = bf16_to_f32(qr[v]);
+    }
+    float kd[2][VPL], vd[2][VPL];  // this wave's first two draft keys / values
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int j = wave + 4 * i;
+        const int jj = j <= di ? j : 0;
+        const uint16_t *kr = p.k_ext + (int64_t)(qo + jj) * p.ke_s0 + (int64_t)kvh * p.ke_s1 + d0;
+        const uint16_t *vr = p.v_ext + (int64_t)(qo + jj) * p.ve_s0 + (int64_t)kvh * p.ve_s1 + d0;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) {
+            kd[i][v] = bf16_to_f32(kr[v]);
+            vd[i][v] = bf16_to_f32(vr[v]);
+        }
+    }
     float m = -INFINITY;
     for (int s = lane; s < count; s += 64)
         m = fmaxf(m, lse_row[s * lse_step]);
+
+    // ---- (a) prefix ranges: global max / normaliser, then this wave's share ----
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1)
         m = fmaxf(m, __shfl_xor(m, off));
@@ -735,25 +778,20 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const CombineParams p
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1)
             den += __shfl_xor(den, off);
-        // weighted sum of this wave's ranges; iterations are independent, so
-        // their loads issue back to back.  An empty range has weight 0, output 0.
-        const float *o_row = p.part_o + (((int64_t)base * p.h_kv + kvh) * p.rows + r) * D + d0;
-        const int64_t o_step = lse_step * D;
-#pragma unroll 4
-        for (int s = wave; s < count; s += 4) {
+        // An empty range (lse -inf) has weight 0 and output 0.
+#pragma unroll
+        for (int i = 0; i < PRE; ++i) {
+            const float w = expf(lw[i] - m);
+#pragma unroll
+            for (int v = 0; v < VPL; ++v)
+                acc[v] += w * ov[i][v];
+        }
+        for (int s = wave + 4 * PRE; s < count; s += 4) {
             const float w = expf(lse_row[s * lse_step] - m);
             const float *o = o_row + s * o_step;
-            if constexpr (VPL == 4) {
-                const f32x4_t x = *(const f32x4_t *)o;
-                acc[0] += w * x[0];
-                acc[1] += w * x[1];
-                acc[2] += w * x[2];
-                acc[3] += w * x[3];
-            } else {
 #pragma unroll
-                for (int v = 0; v < VPL; ++v)
-                    acc[v] += w * o[v];
-            }
+            for (int v = 0; v < VPL; ++v)
+                acc[v] += w * o[v];
         }
     }
 #pragma unroll
@@ -762,25 +800,32 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const CombineParams p
 
     // ---- (b) causal draft keys j <= di, this wave's j = wave mod 4 ----
     // fp32, query not cast, no k/v scale
-    float qv[VPL];
-    {
-        const uint16_t *qr = p.q + (int64_t)(qo + di) * p.q_s0 + (int64_t)h * p.q_s1 + d0;
-#pragma unroll
-        for (int v = 0; v < VPL; ++v)
-            qv[v] = bf16_to_f32(qr[v]);
-    }
     float od[VPL];
 #pragma unroll
     for (int v = 0; v < VPL; ++v)
         od[v] = 0.0f;
     float md = -INFINITY, dd = 0.0f;
-    for (int j = wave; j <= di; j += 4) {
-        const uint16_t *kr = p.k_ext + (int64_t)(qo + j) * p.ke_s0 + (int64_t)kvh * p.ke_s1 + d0;
-        const uint16_t *vr = p.v_ext + (int64_t)(qo + j) * p.ve_s0 + (int64_t)kvh * p.ve_s1 + d0;
+    for (int j = wave, i = 0; j <= di; j += 4, ++i) {
+        float kj[VPL], vj[VPL];
+        if (i < 2) {
+#pragma unroll
+            for (int v = 0; v < VPL; ++v) {
+                kj[v] = i == 0 ? kd[0][v] : kd[1][v];
+                vj[v] = i == 0 ? vd[0][v] : vd[1][v];
+            }
+        } else {
+            const uint16_t *kr = p.k_ext + (int64_t)(qo + j) * p.ke_s0 + (int64_t)kvh * p.ke_s1 + d0;
+            const uint16_t *vr = p.v_ext + (int64_t)(qo + j) * p.ve_s0 + (int64_t)kvh * p.ve_s1 + d0;
+#pragma unroll
+            for (int v = 0; v < VPL; ++v) {
+                kj[v] = bf16_to_f32(kr[v]);
+                vj[v] = bf16_to_f32(vr[v]);
+            }
+        }
         float dot = 0.0f;
 #pragma unroll
         for (int v = 0; v < VPL; ++v)
-            dot += qv[v] * bf16_to_f32(kr[v]);
+            dot += qv[v] * kj[v];
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1)
             dot += __shfl_xor(dot, off);
@@ -790,7 +835,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const CombineParams p
         const float w = expf(sj - mn);
 #pragma unroll
         for (int v = 0; v < VPL; ++v)
-            od[v] = od[v] * a + w * bf16_to_f32(vr[v]);
+            od[v] = od[v] * a + w * vj[v];
         dd = dd * a + w;
         md = mn;
     }
@@ -841,7 +886,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const CombineParams p
 template <bool FP8, int D>
 static int launch_prefix_qb(const PrefixParams &p, int qblocks, int64_t blocks, hipStream_t s)
 {
-    dim3 grid((unsigned)blocks), block(kThreads);
+    dim3 grid((unsigned)blocks), block(prefix_waves(qblocks) * 64);
     if (qblocks == 1)
         hipLaunchKernelGGL((prefix_kernel<FP8, D, 1>), grid, block, 0, s, p);
     else

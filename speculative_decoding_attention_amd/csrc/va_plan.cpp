@@ -159,10 +159,11 @@ int make_plan(const va_desc_t *d, int32_t l_ext, int32_t num_cus, va_plan_t *pla
         p.mode = 0;
         int64_t c = d->split_tokens;
         if (c == 0) {
-            // Enough ranges that every CU holds kResidentPerCU prefix
+            // Enough ranges that every CU holds its resident prefix
             // workgroups; never fewer than kSplitQuantum tokens per range.
             const int64_t units = (int64_t)d->h_kv * p.row_chunks;
-            const int64_t target = (int64_t)kResidentPerCU * num_cus;
+            const int qb = query_blocks_for(rows < kRowChunk ? (int)rows : kRowChunk);
+            const int64_t target = (int64_t)prefix_resident_per_cu(qb) * num_cus;
             c = (T * units + target - 1) / target;
             c = align_up(c < kSplitQuantum ? kSplitQuantum : c, kSplitQuantum);
             if (c > (1 << 30))
