@@ -112,10 +112,10 @@ typedef struct {
     int32_t row_chunks;      /* rows are processed in chunks of at most 64 */
     int32_t tile_tokens;     /* prefix tokens per LDS tile in the prefix kernel */
     int64_t range_slots;     /* upper bound on prefix ranges over the batch (per KV head) */
-    int64_t prefix_blocks;   /* grid of the prefix kernel (workgroups of 256 threads) */
-    int64_t combine_blocks;  /* grid of the combine kernel (workgroups of 256 threads) */
+    int64_t prefix_blocks;   /* grid of the prefix kernel (workgroups of 256 or 512 threads) */
+    int64_t combine_blocks;  /* grid of the combine kernel (one 64-thread workgroup per output row) */
     size_t workspace_bytes;  /* bytes of workspace the two passes need */
-    size_t partial_bytes;    /* of which: fp32 partial outputs */
+    size_t partial_bytes;    /* of which: bf16 partial outputs (the fp32 log-sum-exps follow) */
 } va_plan_t;
 
 /* Validate a descriptor (host only; no HIP call).

@@ -78,7 +78,7 @@ int prefix_impl(const void *q, const void *k_buf, const void *v_buf, const int32
     p.qo_indptr = qo_indptr;
     p.kv_indptr = kv_indptr;
     p.kv_indices = kv_indices;
-    p.part_o = (float *)workspace;
+    p.part_o = (uint16_t *)workspace;
     p.part_lse = (float *)((char *)workspace + plan.partial_bytes);
     const int eb = desc->kv_dtype == VA_DTYPE_FP8_E4M3FN ? 1 : 2;
     p.q_s0 = desc->q_stride[0];
@@ -118,7 +118,7 @@ int combine_impl(const void *q, const void *k_ext, const void *v_ext, const int3
     c.v_ext = (const uint16_t *)v_ext;
     c.qo_indptr = qo_indptr;
     c.kv_indptr = kv_indptr;
-    c.part_o = (const float *)workspace;
+    c.part_o = (const uint16_t *)workspace;
     c.part_lse = (const float *)((const char *)workspace + plan.partial_bytes);
     c.out = (uint16_t *)out;
     c.q_s0 = desc->q_stride[0];

@@ -14,8 +14,10 @@ namespace va {
 constexpr int kRowChunk = 64;
 // Granule of the pages' equal-split rule (ranges are rounded up to it).
 constexpr int kEvenSplitGranule = 32;
-// Threads per workgroup of the combine kernel (4 wavefronts of 64).
-constexpr int kThreads = 256;
+// The combine kernel runs one wavefront per output row, one row per
+// workgroup (the rows then spread over every CU).
+constexpr int kCombineThreads = 64;
+constexpr int kCombineRowsPerBlock = kCombineThreads / 64;
 // Prefix kernel shape.  A workgroup is one group of 4 waves per 32-row query
 // block.  One query block: 4 waves and a 2-tile LDS ring of K/V tiles
 // (<= 32 KB each), two workgroups per CU (their tiles differ, so no score work
@@ -44,8 +46,8 @@ struct PrefixParams {
     const int32_t *qo_indptr;
     const int32_t *kv_indptr;
     const int64_t *kv_indices;
-    float *part_o;    // [range_slots * h_kv, rows, D] fp32
-    float *part_lse;  // [range_slots * h_kv, rows]    fp32 (natural log)
+    uint16_t *part_o;  // [range_slots * h_kv, rows, D] bf16 (round to nearest even)
+    float *part_lse;   // [range_slots * h_kv, rows]    fp32 (natural log)
     int64_t q_s0, q_s1;        // elements
     uint32_t kb_s0, vb_s0;     // pool row strides, bytes (< 2^32, checked on the host)
     int64_t kb_s1, vb_s1;      // pool head strides, bytes
@@ -61,7 +63,7 @@ struct CombineParams {
     const uint16_t *v_ext;
     const int32_t *qo_indptr;
     const int32_t *kv_indptr;
-    const float *part_o;
+    const uint16_t *part_o;
     const float *part_lse;
     uint16_t *out;
     int64_t q_s0, q_s1, ke_s0, ke_s1, ve_s0, ve_s1, o_s0, o_s1;  // elements

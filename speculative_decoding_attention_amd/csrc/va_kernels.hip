@@ -1,17 +1,17 @@
 // va_kernels.hip -- gfx950 kernels of split-KV target-verify attention.
 //
 // Prefix kernel (the pages' _verify_prefix_stage1, sglang verify_splitkv.py):
-// one workgroup of 4 wavefronts per (prefix range, KV head, row chunk).  All
+// one workgroup per (prefix range, KV head, chunk of <= 64 query rows).  All
 // query rows that share a KV head -- the GQA group times the l_ext draft rows
-// -- form one tile of up to 64 rows, so every K/V byte of the range is read
-// from HBM once for the whole group (the pages launch one program per query
-// head and re-read the range per head).  K/V rows are gathered through
-// kv_indices with 16-byte coalesced loads into registers one tile ahead,
-// converted to bf16 if the pool is fp8, and staged in double-buffered LDS.
-// Scores S^T = K Q^T and the update O^T += V^T P^T run on
-// v_mfma_f32_16x16x32_bf16 with fp32 accumulation; the softmax is the online
-// (running max / running sum) recurrence of the pages, in base 2.  k_scale is
-// folded into the score scale; v_scale multiplies the range's output.
+// -- are one or two 32-row MFMA column blocks, so every K/V byte of the range
+// is read from HBM once for the whole group (the pages launch one program per
+// query head and re-read the range per head).  K/V rows are gathered through
+// kv_indices straight into an LDS ring with global_load_lds_dwordx4; scores
+// run on v_mfma_f32_32x32x16 (bf16, or fp8 on the raw E4M3FN pool bytes), the
+// softmax is the online running-max / running-sum recurrence of the pages in
+// base 2 with k_scale folded into the score scale, and P V runs on the same
+// MFMA with V^T read by the transposing LDS read.  Each range writes its
+// normalised, v_scale-multiplied output (bf16) and natural log-sum-exp.
 //
 // Combine kernel (the pages' _verify_combine_stage2): one wavefront per
 // (sequence, KV head, query row): log-sum-exp merge of the ranges, the causal
@@ -360,7 +360,7 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64) void prefix_kernel(const Pr
     const int64_t slot = cidx * p.h_kv + kvh;
     const int rows = p.rows;
     const int row0 = rc * kRowChunk;
-    float *po = p.part_o + slot * (int64_t)rows * D;
+    uint16_t *po = p.part_o + slot * (int64_t)rows * D;
     float *pl = p.part_lse + slot * (int64_t)rows;
 
     if (rg.start >= rg.end) {
@@ -368,7 +368,7 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64) void prefix_kernel(const Pr
         // exactly 0 and no stale value can leak in.
         const int nr = min(rows - row0, NQB * 32);
         for (int e = tid; e < nr * D; e += NW * 64)
-            po[(int64_t)(row0 + e / D) * D + (e % D)] = 0.0f;
+            po[(int64_t)(row0 + e / D) * D + (e % D)] = 0;
         if (tid < nr)
             pl[row0 + tid] = -INFINITY;
         return;
@@ -655,7 +655,7 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64) void prefix_kernel(const Pr
     }
     wait_vm<0>();  // trailing index copies
 
-    // ---- epilogue: normalised, v_scale-multiplied partial and its lse ----
+    // ---- epilogue: normalised, v_scale-multiplied partial (bf16) and its lse ----
     {
         const float lrow = l_part + swap_halves(l_part);
         const int r = row0 + qbw * 32 + l32;
@@ -667,9 +667,9 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64) void prefix_kernel(const Pr
 #pragma unroll
                     for (int g4 = 0; g4 < 4; ++g4) {
                         const int dv = wg * DWV + db * 32 + 8 * g4 + 4 * half;
-                        const f32x4_t o = {oacc[db][4 * g4] * inv, oacc[db][4 * g4 + 1] * inv,
-                                           oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv};
-                        *(f32x4_t *)(po + (int64_t)r * D + dv) = o;
+                        const u32x2_t o = {pack_bf16x2(oacc[db][4 * g4] * inv, oacc[db][4 * g4 + 1] * inv),
+                                           pack_bf16x2(oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv)};
+                        *(u32x2_t *)(po + (int64_t)r * D + dv) = o;
                     }
             }
             if (wg == 0 && half == 0)
@@ -679,23 +679,57 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64) void prefix_kernel(const Pr
 }
 
 // ---------------------------------------------------------- combine kernel ---
-// One workgroup per output row (sequence b, KV head, query row r).  The four
-// waves split the prefix ranges (s = wave mod 4) and the draft keys
-// (j = wave mod 4); their partial sums meet in LDS and wave 0 merges them.
-// Loads are issued in two dependent rounds only: the index pointers, then
-// every log-sum-exp, this wave's partial outputs and its draft rows at once.
+// One wavefront per output row (sequence b, KV head, query row r).  Loads are issued in two dependent
+// rounds: the index pointers, then every range's log-sum-exp (one per lane),
+// the first PRE partial outputs, the query row and the first PRE_D draft rows
+// at once.  Then: (a) log-sum-exp merge of the ranges, (b) the causal draft
+// block in fp32 (query not cast, no k/v scale), (c) the final two-way merge
+// and a round-to-nearest-even bf16 store.
+template <int VPL>
+__device__ __forceinline__ void load_bf16_row(const uint16_t *src, float (&dst)[VPL])
+{
+    if constexpr (VPL == 4) {
+        const u32x2_t w = *(const u32x2_t *)src;
+        dst[0] = bf16_to_f32(w[0] & 0xffffu);
+        dst[1] = bf16_to_f32(w[0] >> 16);
+        dst[2] = bf16_to_f32(w[1] & 0xffffu);
+        dst[3] = bf16_to_f32(w[1] >> 16);
+    } else if constexpr (VPL == 2) {
+        const uint32_t w = *(const uint32_t *)src;
+        dst[0] = bf16_to_f32(w & 0xffffu);
+        dst[1] = bf16_to_f32(w >> 16);
+    } else {
+        dst[0] = bf16_to_f32(*src);
+    }
+}
+
+__device__ __forceinline__ float wave_sum(float x)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        x += __shfl_xor(x, off);
+    return x;
+}
+
+__device__ __forceinline__ float wave_max(float x)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        x = fmaxf(x, __shfl_xor(x, off));
+    return x;
+}
+
 template <int D>
-__global__ __launch_bounds__(kThreads) void combine_kernel(const CombineParams p)
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(const CombineParams p)
 {
     constexpr int VPL = D / 64;  // elements of D / Dv per lane
-    constexpr int PRE = 8;       // partial outputs per wave loaded up front
-    __shared__ __attribute__((aligned(16))) float s_op[4][D];
-    __shared__ __attribute__((aligned(16))) float s_od[4][D];
-    __shared__ float s_md[4], s_dd[4];
+    constexpr int PRE = 32;      // partial outputs per load batch (the first in round 2)
+    constexpr int PRE_D = 8;     // draft rows loaded in the first round
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int64_t gr = blockIdx.x;
+    const int64_t gr = (int64_t)blockIdx.x * kCombineRowsPerBlock + (threadIdx.x >> 6);
+    if (gr >= (int64_t)p.bs * p.h_kv * p.rows)
+        return;  // padding wave of the last workgroup
     const int r = (int)(gr % p.rows);
     const int64_t t = gr / p.rows;
     const int kvh = (int)(t % p.h_kv);
@@ -710,176 +744,139 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const CombineParams p
     int32_t base, count;
     ranges_of(p.kv_indptr, p.bs, p.mode, p.split_tokens, p.n_splits, b, &base, &count);
 
-    // ---- round 2: everything else ----
-    const float *lse_row = p.part_lse + ((int64_t)base * p.h_kv + kvh) * p.rows + r;
+    // ---- round 2: log-sum-exps, partial outputs, query row, draft rows ----
     const int64_t lse_step = (int64_t)p.h_kv * p.rows;  // next range, same head and row
-    const float *o_row = p.part_o + (((int64_t)base * p.h_kv + kvh) * p.rows + r) * D + d0;
+    const float *lse_row = p.part_lse + ((int64_t)base * p.h_kv + kvh) * p.rows + r;
+    const uint16_t *o_row = p.part_o + (((int64_t)base * p.h_kv + kvh) * p.rows + r) * D + d0;
     const int64_t o_step = lse_step * D;
-    float ov[PRE][VPL], lw[PRE];
+    // Every load below is unconditional: a lane or slot past the sequence's
+    // ranges re-reads a valid address (the query row, or the last range) and
+    // gets weight 0, so the compiler issues all loads before the first wait.
+    const uint16_t *q_row = p.q + (int64_t)(qo + di) * p.q_s0 + (int64_t)h * p.q_s1;
+    const int last = count > 0 ? count - 1 : 0;
+    float lse0 = *(lane < count ? lse_row + lane * lse_step : (const float *)q_row);  // range s = lane
+    lse0 = lane < count ? lse0 : -INFINITY;
+    float ov[PRE][VPL];
 #pragma unroll
-    for (int i = 0; i < PRE; ++i) {
-        const int s = wave + 4 * i;
-        lw[i] = -INFINITY;
-#pragma unroll
-        for (int v = 0; v < VPL; ++v)
-            ov[i][v] = 0.0f;
-        if (s < count) {
-            lw[i] = lse_row[s * lse_step];
-            const float *o = o_row + s * o_step;
-            if constexpr (VPL == 4) {
-                const f32x4_t x = *(const f32x4_t *)o;
-                ov[i][0] = x[0];
-                ov[i][1] = x[1];
-                ov[i][2] = x[2];
-                ov[i][3] = x[3];
-            } else {
-#pragma unroll
-                for (int v = 0; v < VPL; ++v)
-                    ov[i][v] = o[v];
-            }
-        }
-    }
+    for (int i = 0; i < PRE; ++i)
+        load_bf16_row<VPL>(count > 0 ? o_row + (i < count ? i : last) * o_step : q_row + d0, ov[i]);
     float qv[VPL];
-    {
-        const uint16_t *qr = p.q + (int64_t)(qo + di) * p.q_s0 + (int64_t)h * p.q_s1 + d0;
+    load_bf16_row<VPL>(q_row + d0, qv);
+    float kd[PRE_D][VPL], vd[PRE_D][VPL];
 #pragma unroll
-        for (int v = 0; v < VPL; ++v)
-            qv[v] = bf16_to_f32(qr[v]);
+    for (int j = 0; j < PRE_D; ++j) {
+        const int jj = j <= di ? j : 0;  // rows past the causal bound are loaded but unused
+        load_bf16_row<VPL>(p.k_ext + (int64_t)(qo + jj) * p.ke_s0 + (int64_t)kvh * p.ke_s1 + d0, kd[j]);
+        load_bf16_row<VPL>(p.v_ext + (int64_t)(qo + jj) * p.ve_s0 + (int64_t)kvh * p.ve_s1 + d0, vd[j]);
     }
-    float kd[2][VPL], vd[2][VPL];  // this wave's first two draft keys / values
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int j = wave + 4 * i;
-        const int jj = j <= di ? j : 0;
-        const uint16_t *kr = p.k_ext + (int64_t)(qo + jj) * p.ke_s0 + (int64_t)kvh * p.ke_s1 + d0;
-        const uint16_t *vr = p.v_ext + (int64_t)(qo + jj) * p.ve_s0 + (int64_t)kvh * p.ve_s1 + d0;
-#pragma unroll
-        for (int v = 0; v < VPL; ++v) {
-            kd[i][v] = bf16_to_f32(kr[v]);
-            vd[i][v] = bf16_to_f32(vr[v]);
-        }
-    }
-    float m = -INFINITY;
-    for (int s = lane; s < count; s += 64)
-        m = fmaxf(m, lse_row[s * lse_step]);
 
-    // ---- (a) prefix ranges: global max / normaliser, then this wave's share ----
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1)
-        m = fmaxf(m, __shfl_xor(m, off));
+    // ---- (a) prefix ranges ----
+    float m = lse0;
+    for (int s = 64 + lane; s < count; s += 64)
+        m = fmaxf(m, lse_row[s * lse_step]);
+    m = wave_max(m);
     float den = 0.0f;
     float acc[VPL];
 #pragma unroll
     for (int v = 0; v < VPL; ++v)
         acc[v] = 0.0f;
-    if (m > -INFINITY) {
-        for (int s = lane; s < count; s += 64)
-            den += expf(lse_row[s * lse_step] - m);
+    if (m > -INFINITY) {  // an empty range (lse -inf) has weight 0 and output 0
+        float e = lane < count ? __expf(lse0 - m) : 0.0f;
+        for (int s = 64 + lane; s < count; s += 64)
+            e += __expf(lse_row[s * lse_step] - m);
+        den = wave_sum(e);
+        // ranges in batches of PRE: every load of a batch is issued before
+        // any is used; lanes hold the log-sum-exps of 64 ranges at a time
+        float lse_c = lse0;
+        for (int s0 = 0; s0 < count; s0 += PRE) {
+            if (s0 > 0) {
+                if ((s0 & 63) == 0) {
+                    const int sl = s0 + lane;
+                    lse_c = lse_row[(sl < count ? sl : last) * lse_step];
+                    lse_c = sl < count ? lse_c : -INFINITY;
+                }
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1)
-            den += __shfl_xor(den, off);
-        // An empty range (lse -inf) has weight 0 and output 0.
+                for (int i = 0; i < PRE; ++i)
+                    load_bf16_row<VPL>(o_row + (s0 + i < count ? s0 + i : last) * o_step, ov[i]);
+            }
 #pragma unroll
-        for (int i = 0; i < PRE; ++i) {
-            const float w = expf(lw[i] - m);
+            for (int i = 0; i < PRE; ++i) {
+                const float w = __expf(__shfl(lse_c, (s0 & 63) + i) - m);  // 0 past count
 #pragma unroll
-            for (int v = 0; v < VPL; ++v)
-                acc[v] += w * ov[i][v];
-        }
-        for (int s = wave + 4 * PRE; s < count; s += 4) {
-            const float w = expf(lse_row[s * lse_step] - m);
-            const float *o = o_row + s * o_step;
-#pragma unroll
-            for (int v = 0; v < VPL; ++v)
-                acc[v] += w * o[v];
+                for (int v = 0; v < VPL; ++v)
+                    acc[v] += w * ov[i][v];
+            }
         }
     }
-#pragma unroll
-    for (int v = 0; v < VPL; ++v)
-        s_op[wave][d0 + v] = acc[v];
 
-    // ---- (b) causal draft keys j <= di, this wave's j = wave mod 4 ----
-    // fp32, query not cast, no k/v scale
+    // ---- (b) causal draft keys j <= di: fp32, query not cast, no k/v scale ----
+    float sj[PRE_D];
+#pragma unroll
+    for (int j = 0; j < PRE_D; ++j) {
+        float dot = 0.0f;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v)
+            dot += qv[v] * kd[j][v];
+        sj[j] = dot;
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+#pragma unroll
+        for (int j = 0; j < PRE_D; ++j)
+            sj[j] += __shfl_xor(sj[j], off);
+    float md = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < PRE_D; ++j) {
+        sj[j] *= p.sm_scale;
+        if (j <= di)
+            md = fmaxf(md, sj[j]);
+    }
+    float dd = 0.0f;
     float od[VPL];
 #pragma unroll
     for (int v = 0; v < VPL; ++v)
         od[v] = 0.0f;
-    float md = -INFINITY, dd = 0.0f;
-    for (int j = wave, i = 0; j <= di; j += 4, ++i) {
-        float kj[VPL], vj[VPL];
-        if (i < 2) {
 #pragma unroll
-            for (int v = 0; v < VPL; ++v) {
-                kj[v] = i == 0 ? kd[0][v] : kd[1][v];
-                vj[v] = i == 0 ? vd[0][v] : vd[1][v];
-            }
-        } else {
-            const uint16_t *kr = p.k_ext + (int64_t)(qo + j) * p.ke_s0 + (int64_t)kvh * p.ke_s1 + d0;
-            const uint16_t *vr = p.v_ext + (int64_t)(qo + j) * p.ve_s0 + (int64_t)kvh * p.ve_s1 + d0;
+    for (int j = 0; j < PRE_D; ++j) {
+        if (j <= di) {
+            const float w = __expf(sj[j] - md);
+            dd += w;
 #pragma unroll
-            for (int v = 0; v < VPL; ++v) {
-                kj[v] = bf16_to_f32(kr[v]);
-                vj[v] = bf16_to_f32(vr[v]);
-            }
+            for (int v = 0; v < VPL; ++v)
+                od[v] += w * vd[j][v];
         }
+    }
+    // draft rows beyond the preloaded ones (l_ext > PRE_D): online update
+    for (int j = PRE_D; j <= di; ++j) {
+        float kj[VPL], vj[VPL];
+        load_bf16_row<VPL>(p.k_ext + (int64_t)(qo + j) * p.ke_s0 + (int64_t)kvh * p.ke_s1 + d0, kj);
+        load_bf16_row<VPL>(p.v_ext + (int64_t)(qo + j) * p.ve_s0 + (int64_t)kvh * p.ve_s1 + d0, vj);
         float dot = 0.0f;
 #pragma unroll
         for (int v = 0; v < VPL; ++v)
             dot += qv[v] * kj[v];
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1)
-            dot += __shfl_xor(dot, off);
-        const float sj = dot * p.sm_scale;
-        const float mn = fmaxf(md, sj);
-        const float a = expf(md - mn);
-        const float w = expf(sj - mn);
+        const float s = wave_sum(dot) * p.sm_scale;
+        const float mn = fmaxf(md, s);
+        const float a = __expf(md - mn);
+        const float w = __expf(s - mn);
 #pragma unroll
         for (int v = 0; v < VPL; ++v)
             od[v] = od[v] * a + w * vj[v];
         dd = dd * a + w;
         md = mn;
     }
-#pragma unroll
-    for (int v = 0; v < VPL; ++v)
-        s_od[wave][d0 + v] = od[v];
-    if (lane == 0) {
-        s_md[wave] = md;
-        s_dd[wave] = dd;
-    }
-    __syncthreads();
-    if (wave != 0)
-        return;
 
-    // ---- (c) merge the waves' shares; final prefix / draft merge; bf16 store ----
-    float mdx = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < 4; ++w)
-        mdx = fmaxf(mdx, s_md[w]);
-    float sw[4], ddx = 0.0f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        sw[w] = s_md[w] == -INFINITY ? 0.0f : expf(s_md[w] - mdx);
-        ddx += sw[w] * s_dd[w];
-    }
-    const float lse_d = mdx + logf(ddx);
-    const float lse_p = den > 0.0f ? m + logf(den) : -INFINITY;
-    const float mm = fmaxf(lse_p, lse_d);
-    const float wp = expf(lse_p - mm);
-    const float wd = expf(lse_d - mm);
-    const float inv = 1.0f / (wp + wd);
-    const float cp = den > 0.0f ? wp / den : 0.0f;  // prefix partial sums -> output
-    const float cd = wd / ddx;                      // draft partial sums -> output
+    // ---- (c) final merge of the prefix and draft parts; bf16 store ----
+    // out = (acc + e^(m_d - M) * od) / (den + e^(m_d - M) * dd) with the prefix
+    // terms taken relative to e^(m - M), M the larger of m and m_d
+    const float mm = fmaxf(m, md);
+    const float wp = den > 0.0f ? __expf(m - mm) : 0.0f;
+    const float wd = __expf(md - mm);
+    const float inv = 1.0f / (wp * den + wd * dd);
     uint16_t *orow = p.out + (int64_t)(qo + di) * p.o_s0 + (int64_t)h * p.o_s1 + d0;
 #pragma unroll
-    for (int v = 0; v < VPL; ++v) {
-        float sp = 0.0f, sd = 0.0f;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            sp += s_op[w][d0 + v];
-            sd += sw[w] * s_od[w][d0 + v];
-        }
-        orow[v] = (uint16_t)f32_to_bf16_rne((sp * cp + sd * cd) * inv);
-    }
+    for (int v = 0; v < VPL; ++v)
+        orow[v] = (uint16_t)f32_to_bf16_rne((wp * acc[v] + wd * od[v]) * inv);
 }
 
 // ----------------------------------------------------------------- launch ---
@@ -915,7 +912,7 @@ int launch_prefix(const PrefixParams &p, int head_dim, bool kv_fp8, int qblocks,
 int launch_combine(const CombineParams &p, int head_dim, int64_t blocks, void *stream)
 {
     hipStream_t s = (hipStream_t)stream;
-    dim3 grid((unsigned)blocks), block(kThreads);
+    dim3 grid((unsigned)blocks), block(kCombineThreads);
     switch (head_dim) {
     case 64: hipLaunchKernelGGL((combine_kernel<64>), grid, block, 0, s, p); break;
     case 128: hipLaunchKernelGGL((combine_kernel<128>), grid, block, 0, s, p); break;

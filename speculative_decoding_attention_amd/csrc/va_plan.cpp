@@ -175,10 +175,11 @@ int make_plan(const va_desc_t *d, int32_t l_ext, int32_t num_cus, va_plan_t *pla
     }
     const int64_t slots = p.range_slots * d->h_kv;
     p.prefix_blocks = slots * p.row_chunks;
-    p.combine_blocks = (int64_t)d->bs * d->h_kv * rows;  // one workgroup per output row
+    // one wavefront per output row
+    p.combine_blocks = ((int64_t)d->bs * d->h_kv * rows + kCombineRowsPerBlock - 1) / kCombineRowsPerBlock;
     if (p.prefix_blocks > INT32_MAX || p.combine_blocks > INT32_MAX || p.range_slots > INT32_MAX)
         return fail(VA_ERR_SIZE, "grid too large (%lld prefix workgroups)", (long long)p.prefix_blocks);
-    const int64_t o_bytes = align_up(slots * rows * d->v_head_dim * 4, 256);
+    const int64_t o_bytes = align_up(slots * rows * d->v_head_dim * 2, 256);  // bf16 partials
     const int64_t l_bytes = align_up(slots * rows * 4, 256);
     p.partial_bytes = (size_t)o_bytes;
     p.workspace_bytes = (size_t)(o_bytes + l_bytes);

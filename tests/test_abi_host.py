@@ -106,7 +106,7 @@ def test_plan_headline_shapes():
     assert plan.mode == 0 and plan.split_tokens == 256
     assert plan.rows == 32 and plan.row_chunks == 1 and plan.tile_tokens == 32
     assert plan.range_slots >= 8 * 8192 // 256
-    assert plan.workspace_bytes >= plan.range_slots * 2 * 32 * 257 * 4
+    assert plan.workspace_bytes >= plan.range_slots * 2 * 32 * (256 * 2 + 4)
 
 
 @pytest.mark.parametrize("seed", range(5))
