@@ -103,12 +103,26 @@ struct Range {
     bool valid;
 };
 
+// Index pointers of 64 consecutive sequences b0 + lane (clamped to the last
+// sequence so that every load is in bounds and unconditional: the compiler
+// then issues all three before the first wait).
+struct SeqChunk {
+    int32_t k0, k1, q0;  // kv_indptr[b], kv_indptr[b + 1], qo_indptr[b]
+};
+
+__device__ __forceinline__ SeqChunk load_seq_chunk(const int32_t *kv_indptr, const int32_t *qo_indptr,
+                                                   int32_t bs, int32_t b0)
+{
+    const int32_t b = min(b0 + (int32_t)(threadIdx.x & 63), bs - 1);
+    return SeqChunk{kv_indptr[b], kv_indptr[b + 1], qo_indptr[b]};
+}
+
 // Whole-wave lookup of range `cidx`: the sequence that owns it, its token
-// range, and that sequence's kv_indptr / qo_indptr entries (read by the same
-// loads as the scan, so no second round trip).
+// range, and that sequence's kv_indptr / qo_indptr entries.  `first` holds
+// the index pointers of sequences 0..63, loaded by the caller ahead of time.
 __device__ __forceinline__ Range locate_range(const int32_t *kv_indptr, const int32_t *qo_indptr,
                                               int32_t bs, int32_t mode, int32_t split_tokens,
-                                              int32_t n_splits, int64_t cidx)
+                                              int32_t n_splits, int64_t cidx, const SeqChunk &first)
 {
     Range r = {0, 0, 0, 0, 0, false};
     if (mode == 1) {
@@ -131,10 +145,9 @@ __device__ __forceinline__ Range locate_range(const int32_t *kv_indptr, const in
     const int lane = threadIdx.x & 63;
     int64_t cum = 0;
     for (int32_t b0 = 0; b0 < bs; b0 += 64) {
+        const SeqChunk c = b0 == 0 ? first : load_seq_chunk(kv_indptr, qo_indptr, bs, b0);
         const int32_t b = b0 + lane;
-        const int32_t k0 = b < bs ? kv_indptr[b] : 0;
-        const int32_t n = b < bs ? kv_indptr[b + 1] - k0 : 0;
-        const int32_t q0 = b < bs ? qo_indptr[b] : 0;
+        const int32_t n = b < bs ? c.k1 - c.k0 : 0;
         const int32_t nch = (n + split_tokens - 1) / split_tokens;
         int32_t incl = nch;
 #pragma unroll
@@ -146,15 +159,15 @@ __device__ __forceinline__ Range locate_range(const int32_t *kv_indptr, const in
         const int32_t total = __shfl(incl, 63);
         if (cidx < cum + total) {
             const uint64_t hit = __ballot(cum + incl > cidx);
-            const int first = __ffsll((unsigned long long)hit) - 1;
-            const int32_t excl = __shfl(incl - nch, first);
-            const int32_t nf = __shfl(n, first);
-            const int32_t c = (int32_t)(cidx - cum - excl);
-            r.b = b0 + first;
-            r.start = c * split_tokens;
+            const int first_hit = __ffsll((unsigned long long)hit) - 1;
+            const int32_t excl = __shfl(incl - nch, first_hit);
+            const int32_t nf = __shfl(n, first_hit);
+            const int32_t ci = (int32_t)(cidx - cum - excl);
+            r.b = b0 + first_hit;
+            r.start = ci * split_tokens;
             r.end = min(r.start + split_tokens, nf);
-            r.kv_base = __shfl(k0, first);
-            r.qo = __shfl(q0, first);
+            r.kv_base = __shfl(c.k0, first_hit);
+            r.qo = __shfl(c.q0, first_hit);
             r.valid = true;
             return r;
         }
@@ -163,10 +176,11 @@ __device__ __forceinline__ Range locate_range(const int32_t *kv_indptr, const in
     return r;
 }
 
-// First range index and range count of sequence b (whole-wave call).
-__device__ __forceinline__ void ranges_of(const int32_t *kv_indptr, int32_t bs, int32_t mode,
-                                          int32_t split_tokens, int32_t n_splits, int32_t b,
-                                          int32_t *base, int32_t *count)
+// First range index and range count of sequence b (whole-wave call); `first`
+// holds the index pointers of sequences 0..63 (see load_seq_chunk).
+__device__ __forceinline__ void ranges_of(const int32_t *kv_indptr, const int32_t *qo_indptr, int32_t bs,
+                                          int32_t mode, int32_t split_tokens, int32_t n_splits, int32_t b,
+                                          const SeqChunk &first, int32_t *base, int32_t *count)
 {
     if (mode == 1) {
         *base = b * n_splits;
@@ -174,19 +188,20 @@ __device__ __forceinline__ void ranges_of(const int32_t *kv_indptr, int32_t bs, 
         return;
     }
     const int lane = threadIdx.x & 63;
-    int32_t acc = 0;
-    for (int32_t b0 = 0; b0 < b; b0 += 64) {
+    int32_t acc = 0, own = 0;
+    for (int32_t b0 = 0; b0 <= b; b0 += 64) {
+        const SeqChunk c = b0 == 0 ? first : load_seq_chunk(kv_indptr, qo_indptr, bs, b0);
         const int32_t bb = b0 + lane;
-        const int32_t n = bb < b ? kv_indptr[bb + 1] - kv_indptr[bb] : 0;
-        int32_t nch = (n + split_tokens - 1) / split_tokens;
+        const int32_t nch = (c.k1 - c.k0 + split_tokens - 1) / split_tokens;
+        own = bb == b ? nch : own;
+        int32_t before = bb < b ? nch : 0;
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1)
-            nch += __shfl_xor(nch, off);
-        acc += nch;
+            before += __shfl_xor(before, off);
+        acc += before;
     }
-    const int32_t n = kv_indptr[b + 1] - kv_indptr[b];
     *base = acc;
-    *count = (n + split_tokens - 1) / split_tokens;
+    *count = __shfl(own, b & 63);
 }
 
 // ----------------------------------------------------------- prefix kernel ---
@@ -311,7 +326,13 @@ __device__ __forceinline__ uint32_t e4m3_code(float v)
 }
 
 template <bool FP8, int D, int NQB>
-__global__ __launch_bounds__(prefix_waves(NQB) * 64) void prefix_kernel(const PrefixParams p)
+// The leading scalar arguments are what the first memory round trip needs
+// (the range lookup); they are preloaded into SGPRs at wave launch, so the
+// kv_indptr loads issue without waiting for the kernel-argument fetch.  The
+// same fields are also in p.
+__global__ __launch_bounds__(prefix_waves(NQB) * 64) void prefix_kernel(
+    const int32_t *kv_indptr, const int32_t *qo_indptr, int32_t bs, int32_t mode, int32_t split_tokens,
+    int32_t n_splits, int32_t h_kv, int32_t row_chunks, const PrefixParams p)
 {
     using G = PrefixGeom<FP8, D, NQB>;
     constexpr int NW = G::NW;
@@ -349,15 +370,21 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64) void prefix_kernel(const Pr
     const int half = lane >> 5;  // k half of the operands
 
     // ---- work item: (range, KV head, row chunk) ----
-    const int64_t blk = blockIdx.x;
-    const int rc = (int)(blk % p.row_chunks);
-    const int64_t t1 = blk / p.row_chunks;
-    const int kvh = (int)(t1 % p.h_kv);
-    const int64_t cidx = t1 / p.h_kv;
-    const Range rg = locate_range(p.kv_indptr, p.qo_indptr, p.bs, p.mode, p.split_tokens, p.n_splits, cidx);
+    // index pointers of the first 64 sequences, then the remaining kernel
+    // arguments while those loads are in flight
+    const SeqChunk first = load_seq_chunk(kv_indptr, qo_indptr, bs, 0);
+    asm volatile("" ::"s"(p.q), "s"(p.kv_indices), "s"(p.k_buf), "s"(p.v_buf), "s"(p.kb_s1), "s"(p.vb_s1),
+                 "s"(p.kb_s0), "s"(p.vb_s0), "s"(p.q_s0), "s"(p.q_s1), "s"(p.group), "s"(p.l_ext), "s"(p.rows)
+                 : "memory");
+    const uint32_t blk = blockIdx.x;
+    const int rc = (int)(blk % (uint32_t)row_chunks);
+    const uint32_t t1 = blk / (uint32_t)row_chunks;
+    const int kvh = (int)(t1 % (uint32_t)h_kv);
+    const int64_t cidx = t1 / (uint32_t)h_kv;
+    const Range rg = locate_range(kv_indptr, qo_indptr, bs, mode, split_tokens, n_splits, cidx, first);
     if (!rg.valid)
         return;  // surplus slot of the static grid: never read by the combine pass
-    const int64_t slot = cidx * p.h_kv + kvh;
+    const int64_t slot = cidx * h_kv + kvh;
     const int rows = p.rows;
     const int row0 = rc * kRowChunk;
     uint16_t *po = p.part_o + slot * (int64_t)rows * D;
@@ -720,29 +747,36 @@ __device__ __forceinline__ float wave_max(float x)
 }
 
 template <int D>
-__global__ __launch_bounds__(kCombineThreads) void combine_kernel(const CombineParams p)
-{
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(
+    const int32_t *kv_indptr, const int32_t *qo_indptr, int32_t bs, int32_t mode, int32_t split_tokens,
+    int32_t n_splits, int32_t h_kv, int32_t rows, const CombineParams p)
+{  // leading arguments preloaded into SGPRs, as for the prefix kernel
     constexpr int VPL = D / 64;  // elements of D / Dv per lane
     constexpr int PRE = 32;      // partial outputs per load batch (the first in round 2)
     constexpr int PRE_D = 8;     // draft rows loaded in the first round
 
     const int lane = threadIdx.x & 63;
-    const int64_t gr = (int64_t)blockIdx.x * kCombineRowsPerBlock + (threadIdx.x >> 6);
-    if (gr >= (int64_t)p.bs * p.h_kv * p.rows)
+    // the plan keeps bs * h_kv * rows below 2^31
+    const uint32_t gr = blockIdx.x * kCombineRowsPerBlock + (threadIdx.x >> 6);
+    if (gr >= (uint32_t)(bs * h_kv * rows))
         return;  // padding wave of the last workgroup
-    const int r = (int)(gr % p.rows);
-    const int64_t t = gr / p.rows;
-    const int kvh = (int)(t % p.h_kv);
-    const int b = (int)(t / p.h_kv);
+    const int r = (int)(gr % (uint32_t)rows);
+    const uint32_t t = gr / (uint32_t)rows;
+    const int kvh = (int)(t % (uint32_t)h_kv);
+    const int b = (int)(t / (uint32_t)h_kv);
     const int hg = r / p.l_ext;
     const int di = r % p.l_ext;
     const int h = kvh * p.group + hg;
     const int d0 = lane * VPL;
 
     // ---- round 1: where this sequence's rows and ranges are ----
-    const int qo = p.qo_indptr[b];
+    const int qo = qo_indptr[b];
+    const SeqChunk first = load_seq_chunk(kv_indptr, qo_indptr, bs, 0);
+    asm volatile("" ::"s"(p.q), "s"(p.k_ext), "s"(p.v_ext), "s"(p.part_o), "s"(p.part_lse), "s"(p.q_s0),
+                 "s"(p.q_s1), "s"(p.ke_s0), "s"(p.ke_s1), "s"(p.ve_s0), "s"(p.ve_s1), "s"(p.group), "s"(p.l_ext)
+                 : "memory");
     int32_t base, count;
-    ranges_of(p.kv_indptr, p.bs, p.mode, p.split_tokens, p.n_splits, b, &base, &count);
+    ranges_of(kv_indptr, qo_indptr, bs, mode, split_tokens, n_splits, b, first, &base, &count);
 
     // ---- round 2: log-sum-exps, partial outputs, query row, draft rows ----
     const int64_t lse_step = (int64_t)p.h_kv * p.rows;  // next range, same head and row
@@ -885,9 +919,11 @@ static int launch_prefix_qb(const PrefixParams &p, int qblocks, int64_t blocks, 
 {
     dim3 grid((unsigned)blocks), block(prefix_waves(qblocks) * 64);
     if (qblocks == 1)
-        hipLaunchKernelGGL((prefix_kernel<FP8, D, 1>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((prefix_kernel<FP8, D, 1>), grid, block, 0, s, p.kv_indptr, p.qo_indptr, p.bs, p.mode,
+                           p.split_tokens, p.n_splits, p.h_kv, p.row_chunks, p);
     else
-        hipLaunchKernelGGL((prefix_kernel<FP8, D, 2>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((prefix_kernel<FP8, D, 2>), grid, block, 0, s, p.kv_indptr, p.qo_indptr, p.bs, p.mode,
+                           p.split_tokens, p.n_splits, p.h_kv, p.row_chunks, p);
     return (int)hipGetLastError();
 }
 
@@ -914,9 +950,11 @@ int launch_combine(const CombineParams &p, int head_dim, int64_t blocks, void *s
     hipStream_t s = (hipStream_t)stream;
     dim3 grid((unsigned)blocks), block(kCombineThreads);
     switch (head_dim) {
-    case 64: hipLaunchKernelGGL((combine_kernel<64>), grid, block, 0, s, p); break;
-    case 128: hipLaunchKernelGGL((combine_kernel<128>), grid, block, 0, s, p); break;
-    default: hipLaunchKernelGGL((combine_kernel<256>), grid, block, 0, s, p); break;
+#define VA_COMBINE_ARGS p.kv_indptr, p.qo_indptr, p.bs, p.mode, p.split_tokens, p.n_splits, p.h_kv, p.rows, p
+    case 64: hipLaunchKernelGGL((combine_kernel<64>), grid, block, 0, s, VA_COMBINE_ARGS); break;
+    case 128: hipLaunchKernelGGL((combine_kernel<128>), grid, block, 0, s, VA_COMBINE_ARGS); break;
+    default: hipLaunchKernelGGL((combine_kernel<256>), grid, block, 0, s, VA_COMBINE_ARGS); break;
+#undef VA_COMBINE_ARGS
     }
     return (int)hipGetLastError();
 }
