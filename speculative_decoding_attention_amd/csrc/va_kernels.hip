@@ -6,11 +6,12 @@
 // -- are one or two 32-row MFMA column blocks, so every K/V byte of the range
 // is read from HBM once for the whole group (the pages launch one program per
 // query head and re-read the range per head).  K/V rows are gathered through
-// kv_indices straight into an LDS ring with global_load_lds_dwordx4; scores
-// run on v_mfma_f32_32x32x16 (bf16, or fp8 on the raw E4M3FN pool bytes), the
-// softmax is the online running-max / running-sum recurrence of the pages in
-// base 2 with k_scale folded into the score scale, and P V runs on the same
-// MFMA with V^T read by the transposing LDS read.  Each range writes its
+// kv_indices straight into an LDS ring with global_load_lds_dwordx4.  Scores
+// run on v_mfma_f32_32x32x16_bf16 (fp8 pools: the 32x32x64 fp8 MFMA on the raw
+// E4M3FN pool bytes); the softmax is the online running-max / running-sum
+// recurrence of the pages in base 2 with k_scale folded into the score scale;
+// P V runs on the bf16 MFMA with V^T from the transposing LDS reads (fp8 V is
+// widened to bf16 by the hardware conversion).  Each range writes its
 // normalised, v_scale-multiplied output (bf16) and natural log-sum-exp.
 //
 // Combine kernel (the pages' _verify_combine_stage2): one wavefront per
@@ -34,6 +35,8 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -50,36 +53,13 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
-// OCP E4M3FN byte -> bf16 bits (exact: every E4M3FN value is a bf16 value).
-// Exponent field e >= 1: 2^(e-7) * (1 + m/8) -> bf16 exponent e + 120.
-// e == 0: subnormal m * 2^-9.  0x7f / 0xff: NaN.
-__device__ __forceinline__ uint32_t e4m3_to_bf16(uint32_t b)
+// q (bf16, exact in f32) -> nearest E4M3FN value, ties to even, saturating at
+// +-448.  v_cvt_pk_fp8_f32 rounds to nearest even on the OCP grid but turns
+// values beyond 448 into NaN, so finite inputs are clamped first (NaN stays
+// NaN).
+__device__ __forceinline__ float clamp_e4m3_range(float x)
 {
-    const uint32_t em = b & 0x7fu;
-    uint32_t r = (em >= 8u) ? (em << 4) + 0x3c00u
-                            : (__float_as_uint((float)em * 0x1p-9f) >> 16);
-    r = (em == 0x7fu) ? 0x7fc0u : r;
-    return ((b & 0x80u) << 8) | r;
-}
-
-// Round a real to the nearest E4M3FN value (ties to even), saturating at
-// +-448.  Grid spacing is 2^(k-3) in [2^k, 2^(k+1)), 2^-9 below 2^-6.
-__device__ __forceinline__ float round_to_e4m3(float x)
-{
-    const float a = fabsf(x);
-    if (a != a)
-        return x;
-    float r;
-    if (!(a < 448.0f)) {
-        r = 448.0f;
-    } else if (a < 0x1p-6f) {
-        r = rintf(a * 512.0f) * 0x1p-9f;
-    } else {
-        int e;
-        frexpf(a, &e);  // a = f * 2^e, f in [0.5, 1): binade k = e - 1
-        r = ldexpf(rintf(ldexpf(a, 4 - e)), e - 4);
-    }
-    return copysignf(r, x);
+    return x != x ? x : fminf(fmaxf(x, -448.0f), 448.0f);
 }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
@@ -235,18 +215,6 @@ __device__ __forceinline__ void wait_vm()
 // (lgkmcnt 0) before it arrives.  Copies into LDS are covered by wait_vm first.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-__device__ __forceinline__ u32x4_t fp8x8_to_bf16(u32x2_t v)
-{
-    u32x4_t o;
-#pragma unroll
-    for (int w = 0; w < 2; ++w) {
-        const uint32_t x = v[w];
-        o[2 * w + 0] = e4m3_to_bf16(x & 0xffu) | (e4m3_to_bf16((x >> 8) & 0xffu) << 16);
-        o[2 * w + 1] = e4m3_to_bf16((x >> 16) & 0xffu) | (e4m3_to_bf16(x >> 24) << 16);
-    }
-    return o;
-}
-
 template <bool FP8, int D, int NQB>
 struct PrefixGeom {
     static constexpr int NW = prefix_waves(NQB);
@@ -267,23 +235,31 @@ struct PrefixGeom {
     static_assert(TN == tile_tokens_for(D, E), "host and kernel tile rules agree");
 };
 
-// LDS layouts (per ring stage; rows of raw pool bytes, 16-byte chunks):
-//   K: chunk c of token row t sits at chunk c ^ kswz(t), kswz(t) = t & 15 (t & 7
-//      for 8-chunk rows): the score MFMA reads 16 consecutive rows at one
-//      chunk per LDS cycle, which this puts on 16 different bank groups;
+// LDS layouts (per ring stage; rows of raw pool bytes, 16-byte chunks; the
+// 64 LDS banks span 256 bytes):
+//   K: chunk c of token row t sits at chunk c ^ kswz(t).  bf16: kswz(t) =
+//      t & 15 (t & 7 for 8-chunk rows): the score MFMA reads 16 consecutive
+//      rows at one chunk per LDS cycle, which this puts on 16 different bank
+//      groups.  fp8 rows are 64..256 bytes, so rows 256 / row_bytes apart
+//      share their banks: kswz(t) = (t / (256 / row_bytes)) mod chunks spreads
+//      every such set of rows over distinct chunks.
 //   V: chunk c of token row t sits at chunk c ^ vswz(t).  bf16 values are read
 //      with the 16-bit transposing read: 32 lanes cover 4 consecutive rows x 4
 //      chunks, so vswz(t) = (t & 3) << 2 moves each row to its own group of 4
-//      chunks ((t & 1) << 2 for 8-chunk rows); fp8 values are read byte by
-//      byte, vswz(t) = (t >> 2) & 3.
+//      chunks ((t & 1) << 2 for 8-chunk rows).  fp8 values are read with the
+//      8-bit transposing read (16 rows x 32 bytes per instruction) and use
+//      the fp8 K rule.
 // The copies choose, for every LDS chunk, the pool chunk that belongs there.
 //
-// Work split: every wave computes the scores of all query rows of a 32-token
-// sub-tile (v_mfma_f32_32x32x16: tokens x 32 query rows), keeps its own copy
-// of the running max / sum, and accumulates only its share of the output
-// columns.  The score C-layout of one 32 x 32 block is exactly the B operand
-// of two value MFMA k-steps, so probabilities never leave registers and a
-// tile needs a single barrier.  The running max is raised only when a row's
+// Work split: a wave computes the scores of all query rows of its block for a
+// 32-token sub-tile (32x32 MFMA: tokens x 32 query rows), keeps its own
+// running max / sum, and accumulates its share of the output columns.  When a
+// tile holds several sub-tiles (short rows: fp8, D <= 128) the waves of a
+// block take different sub-tiles and all columns, so no score is computed
+// twice; with one sub-tile per tile (bf16, D = 256) they share its scores and
+// split the columns.  The score C-layout of one 32 x 32 block is exactly the
+// B operand of two value MFMA k-steps, so probabilities never leave registers
+// and a tile needs a single barrier.  The running max is raised only when a row's
 // new maximum exceeds it by more than 2^8 (the rescale of the accumulators is
 // then skipped for most tiles); probabilities stay below 2^8, far inside the
 // range of bf16 and fp32.
@@ -292,9 +268,18 @@ __device__ __forceinline__ f32x16_t mfma32x32x16(bf16x8_t a, bf16x8_t b, f32x16_
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ f32x16_t mfma32x32x16_fp8(uint64_t a, uint64_t b, f32x16_t c)
+// fp8 x fp8 (format 0: OCP E4M3FN on both operands), E8M0 scales 127 = 1.0
+__device__ __forceinline__ f32x16_t mfma32x32x64_fp8(i32x8_t a, i32x8_t b, f32x16_t c)
 {
-    return __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8((long)a, (long)b, c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// Two E4M3FN codes (bytes 0,1 or, with HIGH, 2,3 of w) -> two bf16 (exact),
+// packed.
+template <bool HIGH>
+__device__ __forceinline__ uint32_t cvt_e4m3x2_bf16(int w)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HIGH));
 }
 
 // value of lane l ^ 32
@@ -311,25 +296,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
-// E4M3FN code of a value that is already exactly representable (|v| <= 448).
-__device__ __forceinline__ uint32_t e4m3_code(float v)
-{
-    const uint32_t u = __float_as_uint(v);
-    const uint32_t s = (u >> 24) & 0x80u;
-    const float a = fabsf(v);
-    uint32_t c;
-    if (a >= 0x1p-6f)
-        c = ((((u >> 23) & 0xffu) - 120u) << 3) | ((u >> 20) & 7u);  // exponent bias 127 -> 7
-    else
-        c = (uint32_t)(a * 512.0f);                                   // subnormal: m * 2^-9
-    return s | c;
-}
-
-template <bool FP8, int D, int NQB>
 // The leading scalar arguments are what the first memory round trip needs
 // (the range lookup); they are preloaded into SGPRs at wave launch, so the
 // kv_indptr loads issue without waiting for the kernel-argument fetch.  The
 // same fields are also in p.
+template <bool FP8, int D, int NQB>
 __global__ __launch_bounds__(prefix_waves(NQB) * 64) void prefix_kernel(
     const int32_t *kv_indptr, const int32_t *qo_indptr, int32_t bs, int32_t mode, int32_t split_tokens,
     int32_t n_splits, int32_t h_kv, int32_t row_chunks, const PrefixParams p)
@@ -345,11 +316,19 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64) void prefix_kernel(
     constexpr int NKS = D / 16;             // k-steps of the score MFMA
     constexpr int NSUB = TN / 32;           // 32-token sub-tiles per tile
     constexpr int GW = NW / NQB;            // waves per query block
-    constexpr int NPVW = GW < D / 32 ? GW : D / 32;  // waves of a block that own output columns
-    constexpr int DWV = D / NPVW;           // output columns per such wave
-    constexpr int DBW = DWV / 32;           // 32-column blocks per such wave
+    // The waves of a query block split a tile's sub-tiles TS ways and the
+    // output columns CS ways (TS * CS = GW).  Each wave keeps its own running
+    // max / sum; the TS token shares are merged after the last tile.
+    constexpr int TS = GW < NSUB ? GW : NSUB;
+    constexpr int CS = GW / TS;
+    constexpr int DWV = D / CS;             // output columns per wave
+    constexpr int DBW = DWV / 32;           // 32-column blocks per wave
+    static_assert(TS * CS == GW && NSUB % TS == 0, "work split");
     constexpr int KSWZ = (LCH < 16 ? LCH : 16) - 1;
     constexpr int VSWZ_ROWS = LCH >= 16 ? 3 : 1;  // bf16: rows whose 4-chunk groups differ
+    constexpr int SW8_SHIFT = ROWB >= 256 ? 0 : (ROWB == 128 ? 1 : 2);  // fp8: log2(256 / row bytes)
+    auto kswz = [](int r) { return FP8 ? ((r >> SW8_SHIFT) & KSWZ) : (r & KSWZ); };
+    auto vswz = [](int r) { return FP8 ? ((r >> SW8_SHIFT) & KSWZ) : ((r & VSWZ_ROWS) << 2); };
     constexpr float kRescale = 8.0f;        // log2 headroom before the max is raised
     static_assert(NQB == 1 || NQB == 2, "query blocks");
     static_assert(NQB * 32 * D * 2 <= G::STAGE, "query tile fits one ring stage");
@@ -444,9 +423,9 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64) void prefix_kernel(
             const int rl = i * G::RPI + lane / LCH;   // row within this wave's rows
             const int row = wave * RW + rl;           // row within the tile
             const int pc = lane % LCH;                // LDS chunk within the row
-            const int vz = FP8 ? ((row >> 2) & 3) : ((row & VSWZ_ROWS) << 2);
+            const int vz = vswz(row);
             const uint64_t t = (uint64_t)ix[rl];
-            dma16(kbase + t * p.kb_s0 + ((pc ^ (row & KSWZ)) << 4),
+            dma16(kbase + t * p.kb_s0 + ((pc ^ kswz(row)) << 4),
                   __builtin_amdgcn_readfirstlane(st + i * 1024));
             dma16(vbase + t * p.vb_s0 + ((pc ^ vz) << 4),
                   __builtin_amdgcn_readfirstlane(st + G::STAGE_K + i * 1024));
@@ -490,29 +469,48 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64) void prefix_kernel(
     // ---- this wave's query block (waves qbw*GW .. +GW share it) ----
     const int qbw = wave / GW;   // query block of this wave
     const int wg = wave % GW;    // wave within the block's group
+    const int ts = wg % TS;      // token share: sub-tiles ts, ts + TS, ...
+    const int cs = wg / TS;      // column share: columns cs * DWV .. + DWV
 
-    // ---- query operand (B: col = query row, k = d): bf16 or E4M3FN codes ----
-    typedef typename std::conditional<FP8, uint64_t, bf16x8_t>::type qop_t;
-    qop_t qreg[NKS];
+    // ---- query operand (B: col = query row, k = d) ----
+    // bf16: k-step ks holds d = 16 ks + 8 half + 0..7.  fp8: E4M3FN codes of q
+    // rounded to the pool dtype (the prefix dot product uses that q); k-step j
+    // of the 32x32x64 MFMA holds d = 64 j + 32 half + 0..31, and the K operand
+    // uses the same d, so the k order inside the instruction does not matter.
+    constexpr int NQR = FP8 ? D / 64 : NKS;
+    typedef typename std::conditional<FP8, i32x8_t, bf16x8_t>::type qop_t;
+    qop_t qreg[NQR];
     {
         const int rl = qbw * 32 + l32;
         const bool rv = row0 + rl < rows;
         const uint8_t *qrow = s_ring + (NBUF - 1) * G::STAGE + (rv ? rl : 0) * D * 2;
+        if constexpr (FP8) {
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            u32x4_t raw = *(const u32x4_t *)(qrow + (ks * 2 + half) * 16);
-            if (!rv)
-                raw = u32x4_t{0u, 0u, 0u, 0u};
-            if constexpr (FP8) {
-                // the prefix dot product uses q rounded to the pool dtype
-                uint64_t codes = 0;
+            for (int j = 0; j < NQR; ++j) {
+                i32x8_t codes;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const uint32_t h = (raw[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-                    codes |= (uint64_t)e4m3_code(round_to_e4m3(bf16_to_f32(h))) << (8 * e);
+                for (int c = 0; c < 4; ++c) {  // 16-byte chunk of 8 bf16 values
+                    u32x4_t raw = *(const u32x4_t *)(qrow + (8 * j + 4 * half + c) * 16);
+                    if (!rv)
+                        raw = u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+                    for (int w = 0; w < 2; ++w) {  // 4 codes per dword
+                        const float x0 = clamp_e4m3_range(bf16_to_f32(raw[2 * w] & 0xffffu));
+                        const float x1 = clamp_e4m3_range(bf16_to_f32(raw[2 * w] >> 16));
+                        const float x2 = clamp_e4m3_range(bf16_to_f32(raw[2 * w + 1] & 0xffffu));
+                        const float x3 = clamp_e4m3_range(bf16_to_f32(raw[2 * w + 1] >> 16));
+                        const int d = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+                        codes[2 * c + w] = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, d, true);
+                    }
                 }
-                qreg[ks] = codes;
-            } else {
+                qreg[j] = codes;
+            }
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                u32x4_t raw = *(const u32x4_t *)(qrow + (ks * 2 + half) * 16);
+                if (!rv)
+                    raw = u32x4_t{0u, 0u, 0u, 0u};
                 qreg[ks] = as_bf16x8(raw);
             }
         }
@@ -524,7 +522,6 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64) void prefix_kernel(
 #pragma unroll
     for (int db = 0; db < DBW; ++db)
         oacc[db] = f32x16_t{};
-    const bool pv_wave = wg < NPVW;
 
     const float qk_scale = p.qk_scale_log2;
     for (int t = 0; t < nt; ++t) {
@@ -566,16 +563,20 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64) void prefix_kernel(
             f32x16_t sc = {}, sc2 = {};
             const int krow = sub * 32 + l32;
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
+            for (int ks = 0; ks < NQR; ++ks) {
                 if constexpr (FP8) {
-                    const int ch = ks ^ (krow & KSWZ);
-                    const uint64_t a = *(const uint64_t *)(K + krow * ROWB + (ch << 4) + half * 8);
+                    // d = 64 ks + 32 half + 0..31: chunks 4 ks + 2 half, +1
+                    const int c0 = 4 * ks + 2 * half;
+                    const u32x4_t lo = *(const u32x4_t *)(K + krow * ROWB + ((c0 ^ kswz(krow)) << 4));
+                    const u32x4_t hi = *(const u32x4_t *)(K + krow * ROWB + (((c0 + 1) ^ kswz(krow)) << 4));
+                    const i32x8_t a = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                       (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
                     if (ks & 1)
-                        sc2 = mfma32x32x16_fp8(a, qreg[ks], sc2);
+                        sc2 = mfma32x32x64_fp8(a, qreg[ks], sc2);
                     else
-                        sc = mfma32x32x16_fp8(a, qreg[ks], sc);
+                        sc = mfma32x32x64_fp8(a, qreg[ks], sc);
                 } else {
-                    const int ch = (ks * 2 + half) ^ (krow & KSWZ);
+                    const int ch = (ks * 2 + half) ^ kswz(krow);
                     const bf16x8_t a = as_bf16x8(*(const u32x4_t *)(K + krow * ROWB + (ch << 4)));
                     if (ks & 1)
                         sc2 = mfma32x32x16(a, qreg[ks], sc2);
@@ -622,29 +623,30 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64) void prefix_kernel(
             l_part += rs;
 
             // ---- O^T[dv][query row] += V^T P^T over this wave's columns ----
-            if (pv_wave) {
+            {
 #pragma unroll
                 for (int db = 0; db < DBW; ++db) {
-                    const int cb = wg * DWV + db * 32;  // first column of the block
+                    const int cb = cs * DWV + db * 32;  // first column of the block
 #pragma unroll
                     for (int kh = 0; kh < 2; ++kh) {    // 16 tokens per value k-step
                         u32x4_t a;
                         if constexpr (FP8) {
-                            const int dv = cb + l32;
-                            uint32_t w4[4];
-#pragma unroll
-                            for (int i2 = 0; i2 < 4; ++i2) {
-                                uint32_t pair = 0;
-#pragma unroll
-                                for (int hh = 0; hh < 2; ++hh) {
-                                    const int s = 2 * i2 + hh;
-                                    const int tok = sub * 32 + kh * 16 + 8 * (s >> 2) + 4 * half + (s & 3);
-                                    const int pc = (dv >> 4) ^ ((tok >> 2) & 3);
-                                    pair |= e4m3_to_bf16(V[tok * ROWB + (pc << 4) + (dv & 15)]) << (16 * hh);
-                                }
-                                w4[i2] = pair;
-                            }
-                            a = u32x4_t{w4[0], w4[1], w4[2], w4[3]};
+                            // 8-bit transposing read: in each 16-lane group,
+                            // input lane 2t+u points at row R(t), columns
+                            // c0 + 8u .. +7; output lane j receives column
+                            // c0 + j of rows R(0..7), here the k-slots of the
+                            // value operand (tokens 4*half + {0..3, 8..11})
+                            const int g16 = lane & 15;
+                            const int t8 = g16 >> 1;
+                            const int col = cb + 16 * ((lane >> 4) & 1) + 8 * (g16 & 1);
+                            const int tok = sub * 32 + kh * 16 + 4 * half + (t8 < 4 ? t8 : t8 + 4);
+                            const int pc = (col >> 4) ^ vswz(tok);
+                            const i32x2_t raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                                (__attribute__((address_space(3))) i32x2_t *)(V + tok * ROWB + (pc << 4) + (col & 15)));
+                            // E4M3FN -> bf16 is exact; the hardware conversion
+                            // decodes the OCP format
+                            a = u32x4_t{cvt_e4m3x2_bf16<false>(raw[0]), cvt_e4m3x2_bf16<true>(raw[0]),
+                                        cvt_e4m3x2_bf16<false>(raw[1]), cvt_e4m3x2_bf16<true>(raw[1])};
                         } else {
                             // transposing reads: input lane 4t+u of each 16-lane
                             // group points at row T(t), columns 4u..4u+3; output
@@ -654,7 +656,7 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64) void prefix_kernel(
 #pragma unroll
                             for (int r = 0; r < 2; ++r) {
                                 const int tok = sub * 32 + kh * 16 + 8 * r + 4 * half + (g16 >> 2);
-                                const int pc = (col >> 3) ^ ((tok & VSWZ_ROWS) << 2);
+                                const int pc = (col >> 3) ^ vswz(tok);
                                 const uint8_t *src = V + tok * ROWB + (pc << 4) + (col & 7) * 2;
                                 const i16x4_t v4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                                     (__attribute__((address_space(3))) i16x4_t *)(src));
@@ -670,7 +672,8 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64) void prefix_kernel(
             }
         };
 #pragma unroll
-        for (int sub = 0; sub < NSUB; ++sub) {
+        for (int i = 0; i < NSUB / TS; ++i) {
+            const int sub = ts + i * TS;
             const int tok0 = t * TN + sub * 32;
             if (tok0 >= len)
                 break;  // rest of the last tile is past the range
@@ -681,27 +684,80 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64) void prefix_kernel(
         }
     }
     wait_vm<0>();  // trailing index copies
+    float lrow = l_part + swap_halves(l_part);
 
-    // ---- epilogue: normalised, v_scale-multiplied partial (bf16) and its lse ----
-    {
-        const float lrow = l_part + swap_halves(l_part);
-        const int r = row0 + qbw * 32 + l32;
-        if (r < rows) {
-            if (pv_wave) {
-                const float inv = p.v_scale / lrow;
+    // ---- merge the token shares: waves ts > 0 hand (max, sum, O) to ts = 0 ----
+    // Slots live in the ring, free once every wave is past the last tile.  A
+    // share that saw no token has max -inf and weight exactly 0; share 0 always
+    // saw the range's first token, so the merged max is finite.
+    if constexpr (TS > 1) {
+        // slot: max[32], sum[32], O[32 rows][DWV + 4] (rows padded by 4 floats
+        // so that the 16-byte accesses of 64 lanes spread over all banks)
+        constexpr int OST = DWV + 4;
+        constexpr int SLOT = 64 + 32 * OST;
+        static_assert(NQB * (TS - 1) * CS * SLOT * 4 <= NBUF * G::STAGE, "merge slots fit the ring");
+        float *slots = (float *)s_ring;
+        lds_barrier();
+        if (ts > 0) {
+            float *sl = slots + ((qbw * (TS - 1) + ts - 1) * CS + cs) * SLOT;
+            if (half == 0) {
+                sl[l32] = m_ref;
+                sl[32 + l32] = lrow;
+            }
+#pragma unroll
+            for (int db = 0; db < DBW; ++db)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4)
+                    *(f32x4_t *)(sl + 64 + l32 * OST + db * 32 + 8 * g4 + 4 * half) =
+                        f32x4_t{oacc[db][4 * g4], oacc[db][4 * g4 + 1], oacc[db][4 * g4 + 2], oacc[db][4 * g4 + 3]};
+        }
+        lds_barrier();
+        if (ts == 0) {
+            float mk[TS - 1], mx = m_ref;
+#pragma unroll
+            for (int k = 0; k < TS - 1; ++k) {
+                mk[k] = slots[((qbw * (TS - 1) + k) * CS + cs) * SLOT + l32];
+                mx = fmaxf(mx, mk[k]);
+            }
+            const float a0 = __builtin_amdgcn_exp2f(m_ref - mx);
+            lrow *= a0;
+#pragma unroll
+            for (int db = 0; db < DBW; ++db)
+                oacc[db] *= a0;
+#pragma unroll
+            for (int k = 0; k < TS - 1; ++k) {
+                const float *sl = slots + ((qbw * (TS - 1) + k) * CS + cs) * SLOT;
+                const float ak = __builtin_amdgcn_exp2f(mk[k] - mx);
+                lrow += ak * sl[32 + l32];
 #pragma unroll
                 for (int db = 0; db < DBW; ++db)
 #pragma unroll
                     for (int g4 = 0; g4 < 4; ++g4) {
-                        const int dv = wg * DWV + db * 32 + 8 * g4 + 4 * half;
-                        const u32x2_t o = {pack_bf16x2(oacc[db][4 * g4] * inv, oacc[db][4 * g4 + 1] * inv),
-                                           pack_bf16x2(oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv)};
-                        *(u32x2_t *)(po + (int64_t)r * D + dv) = o;
+                        const f32x4_t o = *(const f32x4_t *)(sl + 64 + l32 * OST + db * 32 + 8 * g4 + 4 * half);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            oacc[db][4 * g4 + e] += ak * o[e];
                     }
             }
-            if (wg == 0 && half == 0)
-                pl[r] = (m_ref + __log2f(lrow)) * kLn2;
+            m_ref = mx;
         }
+    }
+
+    // ---- epilogue: normalised, v_scale-multiplied partial (bf16) and its lse ----
+    const int r = row0 + qbw * 32 + l32;
+    if (ts == 0 && r < rows) {
+        const float inv = p.v_scale / lrow;
+#pragma unroll
+        for (int db = 0; db < DBW; ++db)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int dv = cs * DWV + db * 32 + 8 * g4 + 4 * half;
+                const u32x2_t o = {pack_bf16x2(oacc[db][4 * g4] * inv, oacc[db][4 * g4 + 1] * inv),
+                                   pack_bf16x2(oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv)};
+                *(u32x2_t *)(po + (int64_t)r * D + dv) = o;
+            }
+        if (cs == 0 && half == 0)
+            pl[r] = (m_ref + __log2f(lrow)) * kLn2;
     }
 }
 
