@@ -78,6 +78,22 @@ def _bind(path):
         I, P, P,
         P, L, L,
     ]
+    lib.oracle_verify_attn_masked.restype = ctypes.c_int
+    lib.oracle_verify_attn_masked.argtypes = [
+        I, I, I, I, I, I,
+        P, L, L, P, L, L, P, L, L,
+        P, L, L, P, L, L,
+        P, P, P,
+        P, P,
+        D, D, D,
+        I, P, P,
+        P, L, L,
+    ]
+    F = ctypes.c_float
+    lib.oracle_append_kv.restype = ctypes.c_int
+    lib.oracle_append_kv.argtypes = [L, I, I, I, I, P, L, L, P, L, L, P, F, F, P, L, L, P, L, L]
+    lib.oracle_build_kv_indices.restype = ctypes.c_int
+    lib.oracle_build_kv_indices.argtypes = [I, P, L, P, P, P, P, P]
     return lib
 
 
@@ -140,14 +156,18 @@ def _np(a, dtype):
 
 
 def verify_attn(q, k_ext, v_ext, k_buf, v_buf, qo_indptr, kv_indptr, kv_indices,
-                sm_scale, k_scale=1.0, v_scale=1.0, kv_fp8=None, select=None, lib=None):
+                sm_scale, k_scale=1.0, v_scale=1.0, kv_fp8=None, select=None, lib=None,
+                custom_mask=None, mask_indptr=None):
     """fp64 oracle output ``[rows, H_Q, Dv]`` (numpy float64).
 
     ``q [rows, H_Q, D]``, ``k_ext [rows, H_KV, D]``, ``v_ext [rows, H_KV, Dv]``
     are bf16 (torch tensors or uint16 bit arrays); ``k_buf [pool, H_KV, D]`` and
     ``v_buf [pool, H_KV, Dv]`` are bf16 or float8_e4m3fn (uint8 codes with
     ``kv_fp8=True``).  ``select`` is an optional list of (b, h) pairs; rows of
-    other pairs come back as NaN.
+    other pairs come back as NaN.  ``custom_mask`` (bytes, nonzero = visible)
+    with ``mask_indptr`` (int64, bs + 1) gives a tree mask over the draft keys:
+    sequence b's mask is row-major ``[n_draft, n_b + n_draft]`` at
+    ``mask_indptr[b]`` and only its draft columns are read.
     """
     lib = lib or _load()
     if kv_fp8 is None:
@@ -179,7 +199,7 @@ def verify_attn(q, k_ext, v_ext, k_buf, v_buf, qo_indptr, kv_indptr, kv_indices,
     def ptr(a):
         return a.ctypes.data_as(ctypes.c_void_p)
 
-    rc = lib.oracle_verify_attn(
+    head = (
         bs, h_q, h_kv, d, dv, 1 if kv_fp8 else 0,
         ptr(qn), qn.strides[0] // qn.itemsize, qn.strides[1] // qn.itemsize,
         ptr(ken), ken.strides[0] // ken.itemsize, ken.strides[1] // ken.itemsize,
@@ -187,10 +207,87 @@ def verify_attn(q, k_ext, v_ext, k_buf, v_buf, qo_indptr, kv_indptr, kv_indices,
         ptr(kbn), kbn.strides[0] // kbn.itemsize, kbn.strides[1] // kbn.itemsize,
         ptr(vbn), vbn.strides[0] // vbn.itemsize, vbn.strides[1] // vbn.itemsize,
         ptr(qo), ptr(kvp), ptr(kvi),
+    )
+    tail = (
         float(sm_scale), float(k_scale), float(v_scale),
         n_sel, ptr(sel_b), ptr(sel_h),
         ptr(out), out.strides[0] // 8, out.strides[1] // 8,
     )
+    if custom_mask is None:
+        rc = lib.oracle_verify_attn(*head, *tail)
+    else:
+        mk = _np(custom_mask, np.uint8)
+        if mk.size == 0:
+            mk = np.zeros(1, np.uint8)
+        mi = _np(mask_indptr, np.int64)
+        rc = lib.oracle_verify_attn_masked(*head, ptr(mk), ptr(mi), *tail)
     if rc != 0:
         raise RuntimeError("oracle_verify_attn failed (rc=%d)" % rc)
     return out
+
+
+def append_kv(k, v, out_cache_loc, k_buf, v_buf, k_scale=1.0, v_scale=1.0, kv_fp8=None, lib=None):
+    """Pool contents after the draft K/V append (copies; inputs untouched).
+
+    ``k [n, H_KV, D]`` / ``v [n, H_KV, Dv]`` bf16; ``k_buf`` / ``v_buf`` bf16 or
+    float8_e4m3fn pools.  Returns (k_bits, v_bits) as uint16 / uint8 arrays of
+    the pool shape.
+    """
+    lib = lib or _load()
+    if kv_fp8 is None:
+        kv_fp8 = hasattr(k_buf, "dtype") and str(k_buf.dtype) == "torch.float8_e4m3fn"
+    kn, vn = _bits16(k), _bits16(v)
+    kb = (_bits8(k_buf) if kv_fp8 else _bits16(k_buf)).copy()
+    vb = (_bits8(v_buf) if kv_fp8 else _bits16(v_buf)).copy()
+    loc = _np(out_cache_loc, np.int64)
+    if loc.size == 0:
+        return kb, vb
+    n, h_kv, d = kn.shape
+    dv = vn.shape[2]
+
+    def ptr(a):
+        return a.ctypes.data_as(ctypes.c_void_p)
+
+    lib.oracle_append_kv(
+        n, h_kv, d, dv, 1 if kv_fp8 else 0,
+        ptr(kn), kn.strides[0] // 2, kn.strides[1] // 2,
+        ptr(vn), vn.strides[0] // 2, vn.strides[1] // 2,
+        ptr(loc), float(k_scale), float(v_scale),
+        ptr(kb), kb.strides[0] // kb.itemsize, kb.strides[1] // kb.itemsize,
+        ptr(vb), vb.strides[0] // vb.itemsize, vb.strides[1] // vb.itemsize)
+    return kb, vb
+
+
+def build_kv_indices(req_to_token, req_pool_indices, seq_lens, kv_start_idx=None, lib=None):
+    """(kv_indptr int32 [bs + 1], kv_indices int64 [sum seq_lens]) from the
+    request-to-token table (int32 [rows, stride])."""
+    lib = lib or _load()
+    rt = _np(req_to_token, np.int32)
+    rp = _np(req_pool_indices, np.int64)
+    sl = _np(seq_lens, np.int32)
+    st = None if kv_start_idx is None else _np(kv_start_idx, np.int32)
+    bs = sl.shape[0]
+    indptr = np.zeros(bs + 1, np.int32)
+    indices = np.zeros(max(int(sl.sum()), 1), np.int64)
+
+    def ptr(a):
+        return a.ctypes.data_as(ctypes.c_void_p) if a is not None else None
+
+    lib.oracle_build_kv_indices(bs, ptr(rt), rt.strides[0] // 4, ptr(rp), ptr(sl), ptr(st),
+                                ptr(indptr), ptr(indices))
+    return indptr, indices[: int(sl.sum())]
+
+
+def expand_block_table(block_table, kv_indptr, page_size):
+    """Token rows of a page-table prefix: token t of sequence b lives in pool
+    row block_table[b, t // page_size] * page_size + t % page_size (the
+    unified-verify block table of aiter_backend.py, the pool viewed as
+    [pages, page_size, H_KV, D]).  Returns int64 kv_indices over all prefix
+    tokens in sequence order."""
+    bt = _np(block_table, np.int64)
+    kvp = _np(kv_indptr, np.int64)
+    out = []
+    for b in range(kvp.shape[0] - 1):
+        t = np.arange(int(kvp[b + 1] - kvp[b]), dtype=np.int64)
+        out.append(bt[b, t // page_size] * page_size + t % page_size)
+    return np.concatenate(out) if out else np.zeros(0, np.int64)

@@ -28,6 +28,18 @@
  *   - the q -> fp8 cast rounds to nearest, ties to even, and saturates to
  *     +-448 (the pages only say the query is converted to the buffer dtype);
  *   - an empty prefix (n_b = 0) gives the draft-only softmax.
+ *
+ * Tree verify (topk > 1; sglang aiter_backend.py passes custom_mask and
+ * mask_indptr with skip_prefix_custom_mask): each sequence's mask is a
+ * row-major [n_draft x (n_b + n_draft)] byte array at mask_indptr[b]; the
+ * prefix columns are not consulted (the prefix stays fully visible) and draft
+ * key j is visible to draft row i where the byte at column n_b + j is nonzero.
+ * Without a mask the draft block is causal.  A row that sees no key at all
+ * gives output 0 (reading: the pages never build such a row).
+ *
+ * Also here: the draft K/V append into the pool (aiter_backend.py,
+ * set_kv_buffer / launch_reshape_and_cache_flash) and the kv_indices build
+ * from req_to_token (create_flashinfer_kv_indices_triton as called there).
  */
 #include <math.h>
 #include <stdint.h>
@@ -110,6 +122,13 @@ uint8_t oracle_f64_to_e4m3fn(double x)
     return (uint8_t)(code | (s << 7));
 }
 
+/* Draft key j visible to draft row i: the row's mask bytes (columns of the
+ * draft keys) when a tree mask is given, else causal. */
+static int draft_visible(const uint8_t *mask_row, int i, int j)
+{
+    return mask_row ? mask_row[j] != 0 : j <= i;
+}
+
 static double pool_elem(const void *buf, int is_fp8, int64_t off)
 {
     if (is_fp8)
@@ -127,7 +146,7 @@ static double pool_elem(const void *buf, int is_fp8, int64_t off)
  * are left untouched.  out is fp64 [rows, h_q, dv] with strides o_s0, o_s1.
  * Returns 0, or -1 on an argument error or allocation failure.
  */
-int oracle_verify_attn(
+static int verify_core(
     int bs, int h_q, int h_kv, int d, int dv, int kv_is_fp8,
     const uint16_t *q, int64_t q_s0, int64_t q_s1,
     const uint16_t *k_ext, int64_t ke_s0, int64_t ke_s1,
@@ -136,6 +155,7 @@ int oracle_verify_attn(
     const void *v_buf, int64_t vb_s0, int64_t vb_s1,
     const int32_t *qo_indptr, const int32_t *kv_indptr,
     const int64_t *kv_indices,
+    const uint8_t *mask, const int64_t *mask_indptr,
     double sm_scale, double k_scale, double v_scale,
     int n_sel, const int32_t *sel_b, const int32_t *sel_h,
     double *out, int64_t o_s0, int64_t o_s1)
@@ -168,6 +188,8 @@ int oracle_verify_attn(
 
         for (int i = 0; i < n_draft; ++i) {
             const int64_t r = row0 + i;
+            const uint8_t *mrow =
+                mask ? mask + mask_indptr[b] + (int64_t)i * (n_pre + n_draft) + n_pre : NULL;
             /* query row, and its copy rounded to the pool element type */
             for (int c = 0; c < d; ++c) {
                 qv[c] = oracle_bf16_to_f64(q[r * q_s0 + (int64_t)h * q_s1 + c]);
@@ -183,8 +205,10 @@ int oracle_verify_attn(
                 sc[j] = sm_scale * k_scale * dot;
                 if (sc[j] > mx) mx = sc[j];
             }
-            /* draft scores: causal j <= i, unscaled, uncast */
-            for (int j = 0; j <= i; ++j) {
+            /* draft scores: visible draft keys (causal: j <= i), unscaled, uncast */
+            for (int j = 0; j < n_draft; ++j) {
+                if (!draft_visible(mrow, i, j))
+                    continue;
                 double dot = 0.0;
                 for (int c = 0; c < d; ++c)
                     dot += qv[c] * oracle_bf16_to_f64(k_ext[(row0 + j) * ke_s0 + (int64_t)g * ke_s1 + c]);
@@ -201,18 +225,136 @@ int oracle_verify_attn(
                 for (int c = 0; c < dv; ++c)
                     acc[c] += w * v_scale * pool_elem(v_buf, kv_is_fp8, t * vb_s0 + (int64_t)g * vb_s1 + c);
             }
-            for (int j = 0; j <= i; ++j) {
+            for (int j = 0; j < n_draft; ++j) {
+                if (!draft_visible(mrow, i, j))
+                    continue;
                 const double w = exp(sc[n_pre + j] - mx);
                 z += w;
                 for (int c = 0; c < dv; ++c)
                     acc[c] += w * oracle_bf16_to_f64(v_ext[(row0 + j) * ve_s0 + (int64_t)g * ve_s1 + c]);
             }
             for (int c = 0; c < dv; ++c)
-                out[r * o_s0 + (int64_t)h * o_s1 + c] = acc[c] / z;
+                out[r * o_s0 + (int64_t)h * o_s1 + c] = z > 0.0 ? acc[c] / z : 0.0;
         }
         free(qv); free(qh); free(sc); free(acc);
     }
     return failed ? -1 : 0;
+}
+
+/* Causal draft block (topk = 1). */
+int oracle_verify_attn(
+    int bs, int h_q, int h_kv, int d, int dv, int kv_is_fp8,
+    const uint16_t *q, int64_t q_s0, int64_t q_s1,
+    const uint16_t *k_ext, int64_t ke_s0, int64_t ke_s1,
+    const uint16_t *v_ext, int64_t ve_s0, int64_t ve_s1,
+    const void *k_buf, int64_t kb_s0, int64_t kb_s1,
+    const void *v_buf, int64_t vb_s0, int64_t vb_s1,
+    const int32_t *qo_indptr, const int32_t *kv_indptr,
+    const int64_t *kv_indices,
+    double sm_scale, double k_scale, double v_scale,
+    int n_sel, const int32_t *sel_b, const int32_t *sel_h,
+    double *out, int64_t o_s0, int64_t o_s1)
+{
+    return verify_core(bs, h_q, h_kv, d, dv, kv_is_fp8, q, q_s0, q_s1, k_ext, ke_s0, ke_s1,
+                       v_ext, ve_s0, ve_s1, k_buf, kb_s0, kb_s1, v_buf, vb_s0, vb_s1,
+                       qo_indptr, kv_indptr, kv_indices, NULL, NULL, sm_scale, k_scale, v_scale,
+                       n_sel, sel_b, sel_h, out, o_s0, o_s1);
+}
+
+/* Tree-masked draft block: mask / mask_indptr as described at the top. */
+int oracle_verify_attn_masked(
+    int bs, int h_q, int h_kv, int d, int dv, int kv_is_fp8,
+    const uint16_t *q, int64_t q_s0, int64_t q_s1,
+    const uint16_t *k_ext, int64_t ke_s0, int64_t ke_s1,
+    const uint16_t *v_ext, int64_t ve_s0, int64_t ve_s1,
+    const void *k_buf, int64_t kb_s0, int64_t kb_s1,
+    const void *v_buf, int64_t vb_s0, int64_t vb_s1,
+    const int32_t *qo_indptr, const int32_t *kv_indptr,
+    const int64_t *kv_indices,
+    const uint8_t *mask, const int64_t *mask_indptr,
+    double sm_scale, double k_scale, double v_scale,
+    int n_sel, const int32_t *sel_b, const int32_t *sel_h,
+    double *out, int64_t o_s0, int64_t o_s1)
+{
+    if (!mask || !mask_indptr)
+        return -1;
+    return verify_core(bs, h_q, h_kv, d, dv, kv_is_fp8, q, q_s0, q_s1, k_ext, ke_s0, ke_s1,
+                       v_ext, ve_s0, ve_s1, k_buf, kb_s0, kb_s1, v_buf, vb_s0, vb_s1,
+                       qo_indptr, kv_indptr, kv_indices, mask, mask_indptr, sm_scale, k_scale,
+                       v_scale, n_sel, sel_b, sel_h, out, o_s0, o_s1);
+}
+
+/*
+ * Draft K/V append (aiter_backend.py: set_kv_buffer, and
+ * launch_reshape_and_cache_flash, which fuses the bf16 -> fp8 cast with the
+ * paged write): row i of k [n, h_kv, d] / v [n, h_kv, dv] (bf16) goes to pool
+ * row loc[i] of every head.  A bf16 pool receives the bits unchanged; an fp8
+ * pool receives the E4M3FN code of x / scale, the quotient formed in fp32
+ * (x and scale as fp32, one correctly rounded division), then rounded to
+ * nearest, ties to even, saturating at +-448 (reading: the pages give the cast
+ * but not its overflow rule; saturation keeps a NaN out of the cache).  Rows
+ * of the pool not named by loc are untouched; a row named twice keeps the
+ * last write (i order).  Strides are in elements.  Returns 0.
+ */
+int oracle_append_kv(
+    int64_t n, int h_kv, int d, int dv, int kv_is_fp8,
+    const uint16_t *k, int64_t k_s0, int64_t k_s1,
+    const uint16_t *v, int64_t v_s0, int64_t v_s1,
+    const int64_t *loc, float k_scale, float v_scale,
+    void *k_buf, int64_t kb_s0, int64_t kb_s1,
+    void *v_buf, int64_t vb_s0, int64_t vb_s1)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        const int64_t t = loc[i];
+        for (int g = 0; g < h_kv; ++g) {
+            for (int c = 0; c < d; ++c) {
+                const uint16_t x = k[i * k_s0 + (int64_t)g * k_s1 + c];
+                const int64_t off = t * kb_s0 + (int64_t)g * kb_s1 + c;
+                if (kv_is_fp8) {
+                    const float y = (float)oracle_bf16_to_f64(x) / k_scale;
+                    ((uint8_t *)k_buf)[off] = oracle_f64_to_e4m3fn((double)y);
+                } else {
+                    ((uint16_t *)k_buf)[off] = x;
+                }
+            }
+            for (int c = 0; c < dv; ++c) {
+                const uint16_t x = v[i * v_s0 + (int64_t)g * v_s1 + c];
+                const int64_t off = t * vb_s0 + (int64_t)g * vb_s1 + c;
+                if (kv_is_fp8) {
+                    const float y = (float)oracle_bf16_to_f64(x) / v_scale;
+                    ((uint8_t *)v_buf)[off] = oracle_f64_to_e4m3fn((double)y);
+                } else {
+                    ((uint16_t *)v_buf)[off] = x;
+                }
+            }
+        }
+    }
+    return 0;
+}
+
+/*
+ * kv_indices from the request-to-token table (aiter_backend.py builds
+ * kv_indptr as the running sum of the per-request lengths and then calls
+ * create_flashinfer_kv_indices_triton with them): for request b and
+ * i < seq_lens[b],
+ *   kv_indices[kv_indptr[b] + i] = req_to_token[req_pool_indices[b] * stride
+ *                                               + start_b + i],
+ * start_b = kv_start_idx[b], or 0 when kv_start_idx is NULL.  kv_indptr
+ * (bs + 1 entries, kv_indptr[0] = 0) is written too.  Returns 0.
+ */
+int oracle_build_kv_indices(
+    int bs, const int32_t *req_to_token, int64_t stride, const int64_t *req_pool_indices,
+    const int32_t *seq_lens, const int32_t *kv_start_idx, int32_t *kv_indptr, int64_t *kv_indices)
+{
+    kv_indptr[0] = 0;
+    for (int b = 0; b < bs; ++b)
+        kv_indptr[b + 1] = kv_indptr[b] + seq_lens[b];
+    for (int b = 0; b < bs; ++b) {
+        const int64_t base = req_pool_indices[b] * stride + (kv_start_idx ? kv_start_idx[b] : 0);
+        for (int32_t i = 0; i < seq_lens[b]; ++i)
+            kv_indices[kv_indptr[b] + i] = req_to_token[base + i];
+    }
+    return 0;
 }
 
 int oracle_max_threads(void)

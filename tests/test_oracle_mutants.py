@@ -29,7 +29,7 @@ MUTANTS = {
     "v_scale applied to draft value": [
         ("acc[c] += w * oracle_bf16_to_f64(v_ext", "acc[c] += w * v_scale * oracle_bf16_to_f64(v_ext")],
     "strict causal bound j < i": [
-        ("for (int j = 0; j <= i; ++j)", "for (int j = 0; j < i; ++j)")],
+        ("return mask_row ? mask_row[j] != 0 : j <= i;", "return mask_row ? mask_row[j] != 0 : j < i;")],
     "draft keys from the query row": [
         ("k_ext[(row0 + j) * ke_s0", "k_ext[(row0 + i) * ke_s0")],
     "heads grouped round-robin": [
