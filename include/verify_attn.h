@@ -158,7 +158,7 @@ VA_API int verify_attn_run(const void *q, const void *k_ext, const void *v_ext,
                            void *stream);
 
 /* Prefix pass only (the pages' _verify_prefix_stage1): writes, for every range
- * and query row, the v_scale-multiplied normalised partial output (fp32) and
+ * and query row, the v_scale-multiplied normalised partial output (bf16) and
  * its natural log-sum-exp into the workspace; an empty range writes output 0
  * and log-sum-exp -inf.  Arguments as for verify_attn_run. */
 VA_API int verify_attn_prefix(const void *q, const void *k_buf, const void *v_buf,
@@ -176,6 +176,63 @@ VA_API int verify_attn_combine(const void *q, const void *k_ext, const void *v_e
                                int32_t l_ext, float sm_scale, void *out,
                                const va_desc_t *desc, void *workspace, size_t workspace_bytes,
                                void *stream);
+
+/* Tree verify (topk > 1): as verify_attn_run / verify_attn_combine, but the
+ * draft block follows a tree mask instead of the causal rule.  Layout of the
+ * mask as sglang's aiter_backend.py builds it for extend attention with
+ * skip_prefix_custom_mask: sequence b's mask is a row-major byte array of
+ * l_ext rows x (n_b + l_ext) columns starting at byte offset mask_indptr[b]
+ * (int64, bs + 1 entries), n_b = kv_indptr[b+1] - kv_indptr[b]; the first n_b
+ * columns (the prefix) are not read -- the prefix stays fully visible -- and
+ * draft key j is visible to draft row i when byte n_b + j of row i is
+ * nonzero.  A row that sees no key at all is written as 0.  l_ext <= 64
+ * (VA_ERR_EXTEND otherwise).  The prefix pass is unchanged. */
+VA_API int verify_attn_run_tree(const void *q, const void *k_ext, const void *v_ext,
+                                const void *k_buf, const void *v_buf,
+                                const int32_t *qo_indptr, const int32_t *kv_indptr,
+                                const int64_t *kv_indices, int32_t l_ext,
+                                float sm_scale, float k_scale, float v_scale,
+                                const uint8_t *custom_mask, const int64_t *mask_indptr, void *out,
+                                const va_desc_t *desc, void *workspace, size_t workspace_bytes,
+                                void *stream);
+
+VA_API int verify_attn_combine_tree(const void *q, const void *k_ext, const void *v_ext,
+                                    const int32_t *qo_indptr, const int32_t *kv_indptr,
+                                    int32_t l_ext, float sm_scale,
+                                    const uint8_t *custom_mask, const int64_t *mask_indptr,
+                                    void *out, const va_desc_t *desc, void *workspace,
+                                    size_t workspace_bytes, void *stream);
+
+/* Draft K/V append into the pool, the step before verify (sglang
+ * aiter_backend.py: set_kv_buffer at out_cache_loc, and
+ * launch_reshape_and_cache_flash, which fuses the bf16 -> fp8 cast with the
+ * paged write).  Row i of k [n_tokens, h_kv, head_dim] and v [n_tokens, h_kv,
+ * v_head_dim] (bf16; strides desc->kext_stride / vext_stride) is written to
+ * pool row out_cache_loc[i] (int64, each in [0, pool)) of k_buf / v_buf
+ * (desc->kv_dtype, strides desc->kbuf_stride / vbuf_stride).  A bf16 pool
+ * receives the bits unchanged (scales ignored); an fp8 pool receives the
+ * E4M3FN code of x / scale, the quotient one correctly rounded fp32 division,
+ * rounded to nearest even and saturating at +-448.  Rows named twice: one of
+ * the writes survives (unordered).  Uses desc->h_kv, head_dim, v_head_dim,
+ * kv_dtype and the four strides only.  n_tokens = 0 is a no-op. */
+VA_API int verify_attn_append_kv(const void *k, const void *v, const int64_t *out_cache_loc,
+                                 int64_t n_tokens, float k_scale, float v_scale,
+                                 void *k_buf, void *v_buf, const va_desc_t *desc, void *stream);
+
+/* kv_indices from the request-to-token table, as sglang's aiter_backend.py
+ * builds them for verify (kv_indptr = running sum of the lengths, then
+ * create_flashinfer_kv_indices_triton): for request b < bs and i < seq_lens[b],
+ *   kv_indices[kv_indptr[b] + i] =
+ *       req_to_token[req_pool_indices[b] * req_to_token_stride + start_b + i]
+ * with start_b = kv_start_idx[b] (or 0 when kv_start_idx is NULL).  Writes
+ * kv_indptr [bs + 1] (int32, kv_indptr[0] = 0) too.  req_to_token is int32,
+ * req_pool_indices int64, seq_lens and kv_start_idx int32.  capacity is the
+ * length of kv_indices (normally the host-known total of seq_lens); entries
+ * beyond it are not written.  One kernel launch; no host synchronisation. */
+VA_API int verify_attn_build_kv_indices(const int32_t *req_to_token, int64_t req_to_token_stride,
+                                        const int64_t *req_pool_indices, const int32_t *seq_lens,
+                                        const int32_t *kv_start_idx, int32_t bs, int64_t capacity,
+                                        int32_t *kv_indptr, int64_t *kv_indices, void *stream);
 
 /* Static text for a status code. */
 VA_API const char *verify_attn_strerror(int code);

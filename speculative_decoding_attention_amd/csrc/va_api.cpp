@@ -110,9 +110,12 @@ int prefix_impl(const void *q, const void *k_buf, const void *v_buf, const int32
 
 int combine_impl(const void *q, const void *k_ext, const void *v_ext, const int32_t *qo_indptr,
                  const int32_t *kv_indptr, int32_t l_ext, float sm_scale, void *out,
-                 const va_desc_t *desc, const va_plan_t &plan, void *workspace, void *stream)
+                 const va_desc_t *desc, const va_plan_t &plan, void *workspace, void *stream,
+                 const uint8_t *mask = nullptr, const int64_t *mask_indptr = nullptr)
 {
     CombineParams c;
+    c.mask = mask;
+    c.mask_indptr = mask_indptr;
     c.q = (const uint16_t *)q;
     c.k_ext = (const uint16_t *)k_ext;
     c.v_ext = (const uint16_t *)v_ext;
@@ -146,6 +149,20 @@ int combine_impl(const void *q, const void *k_ext, const void *v_ext, const int3
     return VA_OK;
 }
 
+// Tree-mask arguments of the *_tree entry points.
+int check_tree(const uint8_t *mask, const int64_t *mask_indptr, int32_t l_ext)
+{
+    const void *ptrs[2] = {mask, mask_indptr};
+    int rc = check_ptrs(ptrs, 2);
+    if (rc != VA_OK)
+        return rc;
+    if (l_ext > kMaxTreeDrafts) {
+        set_error("l_ext = %d; the tree-mask path takes at most %d draft tokens", l_ext, kMaxTreeDrafts);
+        return VA_ERR_EXTEND;
+    }
+    return VA_OK;
+}
+
 }  // namespace
 }  // namespace va
 
@@ -157,8 +174,7 @@ VA_API int verify_attn_prefix(const void *q, const void *k_buf, const void *v_bu
                               float k_scale, float v_scale, const va_desc_t *desc, void *workspace,
                               size_t workspace_bytes, void *stream)
 {
-    va_plan_t plan;
-    int rc = va::make_plan(desc, l_ext, 0, &plan);
+    int rc = va::check_desc(desc, l_ext);  // host checks first: no device query on bad input
     if (rc != VA_OK)
         return rc;
     // kv_indices may be NULL only when there is no prefix token at all
@@ -171,6 +187,9 @@ VA_API int verify_attn_prefix(const void *q, const void *k_buf, const void *v_bu
         return rc;
     if ((rc = va::check_scales(sm_scale, k_scale, v_scale)) != VA_OK)
         return rc;
+    va_plan_t plan;
+    if ((rc = va::make_plan(desc, l_ext, 0, &plan)) != VA_OK)
+        return rc;
     if ((rc = va::check_workspace(plan, workspace, workspace_bytes)) != VA_OK)
         return rc;
     return va::prefix_impl(q, k_buf, v_buf, qo_indptr, kv_indptr, kv_indices, l_ext, sm_scale,
@@ -182,8 +201,7 @@ VA_API int verify_attn_combine(const void *q, const void *k_ext, const void *v_e
                                float sm_scale, void *out, const va_desc_t *desc, void *workspace,
                                size_t workspace_bytes, void *stream)
 {
-    va_plan_t plan;
-    int rc = va::make_plan(desc, l_ext, 0, &plan);
+    int rc = va::check_desc(desc, l_ext);  // host checks first: no device query on bad input
     if (rc != VA_OK)
         return rc;
     const void *ptrs[6] = {q, k_ext, v_ext, qo_indptr, kv_indptr, out};
@@ -193,6 +211,9 @@ VA_API int verify_attn_combine(const void *q, const void *k_ext, const void *v_e
     if ((rc = va::check_align(al, 4)) != VA_OK)
         return rc;
     if ((rc = va::check_scales(sm_scale, 1.0f, 1.0f)) != VA_OK)
+        return rc;
+    va_plan_t plan;
+    if ((rc = va::make_plan(desc, l_ext, 0, &plan)) != VA_OK)
         return rc;
     if ((rc = va::check_workspace(plan, workspace, workspace_bytes)) != VA_OK)
         return rc;
@@ -206,8 +227,7 @@ VA_API int verify_attn_run(const void *q, const void *k_ext, const void *v_ext, 
                            float v_scale, void *out, const va_desc_t *desc, void *workspace,
                            size_t workspace_bytes, void *stream)
 {
-    va_plan_t plan;
-    int rc = va::make_plan(desc, l_ext, 0, &plan);
+    int rc = va::check_desc(desc, l_ext);  // host checks first: no device query on bad input
     if (rc != VA_OK)
         return rc;
     const void *ptrs[9] = {q, k_ext, v_ext, k_buf, v_buf, qo_indptr, kv_indptr,
@@ -219,6 +239,9 @@ VA_API int verify_attn_run(const void *q, const void *k_ext, const void *v_ext, 
         return rc;
     if ((rc = va::check_scales(sm_scale, k_scale, v_scale)) != VA_OK)
         return rc;
+    va_plan_t plan;
+    if ((rc = va::make_plan(desc, l_ext, 0, &plan)) != VA_OK)
+        return rc;
     if ((rc = va::check_workspace(plan, workspace, workspace_bytes)) != VA_OK)
         return rc;
     rc = va::prefix_impl(q, k_buf, v_buf, qo_indptr, kv_indptr, kv_indices, l_ext, sm_scale, k_scale,
@@ -227,6 +250,68 @@ VA_API int verify_attn_run(const void *q, const void *k_ext, const void *v_ext, 
         return rc;
     return va::combine_impl(q, k_ext, v_ext, qo_indptr, kv_indptr, l_ext, sm_scale, out, desc, plan,
                             workspace, stream);
+}
+
+VA_API int verify_attn_combine_tree(const void *q, const void *k_ext, const void *v_ext,
+                                    const int32_t *qo_indptr, const int32_t *kv_indptr, int32_t l_ext,
+                                    float sm_scale, const uint8_t *custom_mask, const int64_t *mask_indptr,
+                                    void *out, const va_desc_t *desc, void *workspace,
+                                    size_t workspace_bytes, void *stream)
+{
+    int rc = va::check_desc(desc, l_ext);  // host checks first: no device query on bad input
+    if (rc != VA_OK)
+        return rc;
+    const void *ptrs[6] = {q, k_ext, v_ext, qo_indptr, kv_indptr, out};
+    if ((rc = va::check_ptrs(ptrs, 6)) != VA_OK)
+        return rc;
+    if ((rc = va::check_tree(custom_mask, mask_indptr, l_ext)) != VA_OK)
+        return rc;
+    const void *al[4] = {q, k_ext, v_ext, out};
+    if ((rc = va::check_align(al, 4)) != VA_OK)
+        return rc;
+    if ((rc = va::check_scales(sm_scale, 1.0f, 1.0f)) != VA_OK)
+        return rc;
+    va_plan_t plan;
+    if ((rc = va::make_plan(desc, l_ext, 0, &plan)) != VA_OK)
+        return rc;
+    if ((rc = va::check_workspace(plan, workspace, workspace_bytes)) != VA_OK)
+        return rc;
+    return va::combine_impl(q, k_ext, v_ext, qo_indptr, kv_indptr, l_ext, sm_scale, out, desc, plan,
+                            workspace, stream, custom_mask, mask_indptr);
+}
+
+VA_API int verify_attn_run_tree(const void *q, const void *k_ext, const void *v_ext, const void *k_buf,
+                                const void *v_buf, const int32_t *qo_indptr, const int32_t *kv_indptr,
+                                const int64_t *kv_indices, int32_t l_ext, float sm_scale, float k_scale,
+                                float v_scale, const uint8_t *custom_mask, const int64_t *mask_indptr,
+                                void *out, const va_desc_t *desc, void *workspace, size_t workspace_bytes,
+                                void *stream)
+{
+    int rc = va::check_desc(desc, l_ext);  // host checks first: no device query on bad input
+    if (rc != VA_OK)
+        return rc;
+    const void *ptrs[9] = {q, k_ext, v_ext, k_buf, v_buf, qo_indptr, kv_indptr,
+                           desc->num_kv_indices > 0 ? (const void *)kv_indices : (const void *)q, out};
+    if ((rc = va::check_ptrs(ptrs, 9)) != VA_OK)
+        return rc;
+    if ((rc = va::check_tree(custom_mask, mask_indptr, l_ext)) != VA_OK)
+        return rc;
+    const void *al[6] = {q, k_ext, v_ext, k_buf, v_buf, out};
+    if ((rc = va::check_align(al, 6)) != VA_OK)
+        return rc;
+    if ((rc = va::check_scales(sm_scale, k_scale, v_scale)) != VA_OK)
+        return rc;
+    va_plan_t plan;
+    if ((rc = va::make_plan(desc, l_ext, 0, &plan)) != VA_OK)
+        return rc;
+    if ((rc = va::check_workspace(plan, workspace, workspace_bytes)) != VA_OK)
+        return rc;
+    rc = va::prefix_impl(q, k_buf, v_buf, qo_indptr, kv_indptr, kv_indices, l_ext, sm_scale, k_scale,
+                         v_scale, desc, plan, workspace, stream);
+    if (rc != VA_OK)
+        return rc;
+    return va::combine_impl(q, k_ext, v_ext, qo_indptr, kv_indptr, l_ext, sm_scale, out, desc, plan,
+                            workspace, stream, custom_mask, mask_indptr);
 }
 
 }  // extern "C"

@@ -26,6 +26,9 @@ constexpr int kCombineRowsPerBlock = kCombineThreads / 64;
 constexpr int prefix_waves(int qblocks) { return qblocks == 1 ? 4 : 8; }
 constexpr int prefix_ring_stages(int qblocks) { return qblocks == 1 ? 2 : 4; }
 constexpr int prefix_resident_per_cu(int qblocks) { return qblocks == 1 ? 2 : 1; }
+// Draft tokens a tree mask may cover (the combine kernel keeps a row's
+// visibility in one 64-bit ballot).
+constexpr int kMaxTreeDrafts = 64;
 // Smallest range the heuristic chooses; ranges are multiples of this.
 constexpr int kSplitQuantum = 64;
 
@@ -66,11 +69,44 @@ struct CombineParams {
     const uint16_t *part_o;
     const float *part_lse;
     uint16_t *out;
+    const uint8_t *mask;          // tree mask bytes, or NULL for the causal draft block
+    const int64_t *mask_indptr;   // [bs + 1] byte offsets of each sequence's mask
     int64_t q_s0, q_s1, ke_s0, ke_s1, ve_s0, ve_s1, o_s0, o_s1;  // elements
     float sm_scale;
     int32_t bs, h_kv, group, l_ext, rows;
     int32_t mode, split_tokens, n_splits;
 };
+
+// Threads per workgroup of the append and kv_indices kernels (va_aux.hip).
+constexpr int kAuxThreads = 256;
+
+struct AppendParams {
+    const uint16_t *k;        // [n, h_kv, D] bf16
+    const uint16_t *v;        // [n, h_kv, Dv] bf16
+    const int64_t *loc;       // [n] pool rows
+    uint8_t *k_buf;           // pool bytes (bf16 or E4M3FN)
+    uint8_t *v_buf;
+    int64_t n;
+    int32_t h_kv;
+    int64_t k_s0, k_s1, v_s0, v_s1;      // elements
+    int64_t kb_s0, kb_s1, vb_s0, vb_s1;  // bytes
+    float k_scale, v_scale;
+};
+
+struct BuildIndicesParams {
+    const int32_t *req_to_token;
+    int64_t rt_stride;               // elements per req_to_token row
+    const int64_t *req_pool_indices;
+    const int32_t *seq_lens;
+    const int32_t *kv_start_idx;     // or NULL
+    int32_t *kv_indptr;              // [bs + 1] out
+    int64_t *kv_indices;             // [capacity] out
+    int64_t capacity;
+    int32_t bs, parts;               // parts: workgroups per request
+};
+
+int launch_append(const AppendParams &p, int head_dim, bool kv_fp8, void *stream);
+int launch_build_kv_indices(const BuildIndicesParams &p, void *stream);
 
 // Launchers (defined in va_kernels.hip).  Return a hipError_t value.
 int launch_prefix(const PrefixParams &p, int head_dim, bool kv_fp8, int qblocks,

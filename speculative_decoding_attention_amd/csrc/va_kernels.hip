@@ -765,9 +765,11 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64) void prefix_kernel(
 // One wavefront per output row (sequence b, KV head, query row r).  Loads are issued in two dependent
 // rounds: the index pointers, then every range's log-sum-exp (one per lane),
 // the first PRE partial outputs, the query row and the first PRE_D draft rows
-// at once.  Then: (a) log-sum-exp merge of the ranges, (b) the causal draft
-// block in fp32 (query not cast, no k/v scale), (c) the final two-way merge
-// and a round-to-nearest-even bf16 store.
+// at once.  Then: (a) log-sum-exp merge of the ranges, (b) the draft block in
+// fp32 (query not cast, no k/v scale) over the visible draft keys -- causal,
+// or a tree mask (aiter_backend.py's custom_mask / mask_indptr with the prefix
+// columns skipped), (c) the final two-way merge and a round-to-nearest-even
+// bf16 store.  A row that sees no key at all is written as 0.
 template <int VPL>
 __device__ __forceinline__ void load_bf16_row(const uint16_t *src, float (&dst)[VPL])
 {
@@ -833,6 +835,11 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
                  : "memory");
     int32_t base, count;
     ranges_of(kv_indptr, qo_indptr, bs, mode, split_tokens, n_splits, b, first, &base, &count);
+    const int L = p.l_ext;
+    int64_t mrow = 0;  // this row's tree-mask bytes for the draft keys
+    if (p.mask)
+        mrow = p.mask_indptr[b] + (int64_t)di * (kv_indptr[b + 1] - kv_indptr[b] + L) +
+               (kv_indptr[b + 1] - kv_indptr[b]);
 
     // ---- round 2: log-sum-exps, partial outputs, query row, draft rows ----
     const int64_t lse_step = (int64_t)p.h_kv * p.rows;  // next range, same head and row
@@ -852,10 +859,18 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
         load_bf16_row<VPL>(count > 0 ? o_row + (i < count ? i : last) * o_step : q_row + d0, ov[i]);
     float qv[VPL];
     load_bf16_row<VPL>(q_row + d0, qv);
+    // visible draft keys j < 64 as bits: mask bytes (one lane per key) or j <= di
+    uint64_t vis;
+    if (p.mask) {
+        const uint8_t byte = p.mask[mrow + (lane < L ? lane : 0)];
+        vis = __ballot(lane < L && byte != 0);
+    } else {
+        vis = di >= 63 ? ~0ull : ((2ull << di) - 1);
+    }
     float kd[PRE_D][VPL], vd[PRE_D][VPL];
 #pragma unroll
     for (int j = 0; j < PRE_D; ++j) {
-        const int jj = j <= di ? j : 0;  // rows past the causal bound are loaded but unused
+        const int jj = j < L ? j : 0;  // rows past the sequence's drafts are loaded but unused
         load_bf16_row<VPL>(p.k_ext + (int64_t)(qo + jj) * p.ke_s0 + (int64_t)kvh * p.ke_s1 + d0, kd[j]);
         load_bf16_row<VPL>(p.v_ext + (int64_t)(qo + jj) * p.ve_s0 + (int64_t)kvh * p.ve_s1 + d0, vd[j]);
     }
@@ -899,7 +914,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
         }
     }
 
-    // ---- (b) causal draft keys j <= di: fp32, query not cast, no k/v scale ----
+    // ---- (b) visible draft keys: fp32, query not cast, no k/v scale ----
     float sj[PRE_D];
 #pragma unroll
     for (int j = 0; j < PRE_D; ++j) {
@@ -918,7 +933,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
 #pragma unroll
     for (int j = 0; j < PRE_D; ++j) {
         sj[j] *= p.sm_scale;
-        if (j <= di)
+        if ((vis >> j) & 1)
             md = fmaxf(md, sj[j]);
     }
     float dd = 0.0f;
@@ -928,7 +943,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
         od[v] = 0.0f;
 #pragma unroll
     for (int j = 0; j < PRE_D; ++j) {
-        if (j <= di) {
+        if ((vis >> j) & 1) {
             const float w = __expf(sj[j] - md);
             dd += w;
 #pragma unroll
@@ -937,7 +952,10 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
         }
     }
     // draft rows beyond the preloaded ones (l_ext > PRE_D): online update
-    for (int j = PRE_D; j <= di; ++j) {
+    const int jend = p.mask ? L : di + 1;
+    for (int j = PRE_D; j < jend; ++j) {
+        if (p.mask && !((vis >> j) & 1))
+            continue;
         float kj[VPL], vj[VPL];
         load_bf16_row<VPL>(p.k_ext + (int64_t)(qo + j) * p.ke_s0 + (int64_t)kvh * p.ke_s1 + d0, kj);
         load_bf16_row<VPL>(p.v_ext + (int64_t)(qo + j) * p.ve_s0 + (int64_t)kvh * p.ve_s1 + d0, vj);
@@ -961,8 +979,9 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     // terms taken relative to e^(m - M), M the larger of m and m_d
     const float mm = fmaxf(m, md);
     const float wp = den > 0.0f ? __expf(m - mm) : 0.0f;
-    const float wd = __expf(md - mm);
-    const float inv = 1.0f / (wp * den + wd * dd);
+    const float wd = dd > 0.0f ? __expf(md - mm) : 0.0f;
+    const float tot = wp * den + wd * dd;
+    const float inv = tot > 0.0f ? 1.0f / tot : 0.0f;
     uint16_t *orow = p.out + (int64_t)(qo + di) * p.o_s0 + (int64_t)h * p.o_s1 + d0;
 #pragma unroll
     for (int v = 0; v < VPL; ++v)

@@ -237,6 +237,6 @@ VA_API const char *verify_attn_strerror(int code)
 
 VA_API const char *verify_attn_last_error(void) { return va::last_error(); }
 
-VA_API int verify_attn_version(void) { return 100; }
+VA_API int verify_attn_version(void) { return 200; }
 
 }  // extern "C"

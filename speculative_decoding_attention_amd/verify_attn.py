@@ -68,8 +68,14 @@ def _load():
     lib.verify_attn_run.argtypes = [P, P, P, P, P, P, P, P, I32, F, F, F, P, DP, P, SZ, P]
     lib.verify_attn_prefix.argtypes = [P, P, P, P, P, P, I32, F, F, F, DP, P, SZ, P]
     lib.verify_attn_combine.argtypes = [P, P, P, P, P, I32, F, P, DP, P, SZ, P]
+    lib.verify_attn_run_tree.argtypes = [P, P, P, P, P, P, P, P, I32, F, F, F, P, P, P, DP, P, SZ, P]
+    lib.verify_attn_combine_tree.argtypes = [P, P, P, P, P, I32, F, P, P, P, DP, P, SZ, P]
+    lib.verify_attn_append_kv.argtypes = [P, P, P, ctypes.c_int64, F, F, P, P, DP, P]
+    lib.verify_attn_build_kv_indices.argtypes = [P, ctypes.c_int64, P, P, P, I32, ctypes.c_int64, P, P, P]
     for name in ("verify_attn_check", "verify_attn_plan", "verify_attn_workspace_bytes",
                  "verify_attn_run", "verify_attn_prefix", "verify_attn_combine",
+                 "verify_attn_run_tree", "verify_attn_combine_tree", "verify_attn_append_kv",
+                 "verify_attn_build_kv_indices",
                  "verify_attn_version"):
         getattr(lib, name).restype = ctypes.c_int
     lib.verify_attn_strerror.argtypes = [ctypes.c_int]
@@ -219,6 +225,82 @@ def verify_attn_combine(q, k_ext, v_ext, qo_indptr, kv_indptr, l_ext, sm_scale, 
         _stream(stream))
     _ok(rc, "verify_attn_combine")
     return out
+
+
+def verify_attn_run_tree(q, k_ext, v_ext, k_buf, v_buf, qo_indptr, kv_indptr, kv_indices, l_ext,
+                         custom_mask, mask_indptr, sm_scale=None, k_scale=1.0, v_scale=1.0, out=None,
+                         workspace=None, split_tokens=0, n_splits=0, stream=None, desc=None):
+    """Tree verify: as verify_attn_run with the draft block under ``custom_mask``
+    (uint8/bool, per-sequence ``[l_ext, n_b + l_ext]`` row-major at
+    ``mask_indptr[b]``, int64; prefix columns not read)."""
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(q.shape[2])
+    if out is None:
+        out = torch.empty(q.shape[0], q.shape[1], v_ext.shape[2], dtype=q.dtype, device=q.device)
+    bs = qo_indptr.shape[0] - 1
+    if desc is None:
+        desc = make_desc(q, k_ext, v_ext, k_buf, v_buf, kv_indices, out, bs, split_tokens, n_splits)
+    if workspace is None:
+        workspace = alloc_workspace(desc, l_ext, q.device)
+    rc = _lib.verify_attn_run_tree(
+        _ptr(q), _ptr(k_ext), _ptr(v_ext), _ptr(k_buf), _ptr(v_buf), _ptr(qo_indptr),
+        _ptr(kv_indptr), _ptr(kv_indices) if kv_indices.numel() else 0, int(l_ext),
+        float(sm_scale), float(k_scale), float(v_scale), _ptr(custom_mask), _ptr(mask_indptr),
+        _ptr(out), ctypes.byref(desc), _ptr(workspace), workspace.numel(), _stream(stream))
+    _ok(rc, "verify_attn_run_tree")
+    return out
+
+
+def verify_attn_combine_tree(q, k_ext, v_ext, qo_indptr, kv_indptr, l_ext, sm_scale, custom_mask,
+                             mask_indptr, out, desc, workspace, stream=None):
+    rc = _lib.verify_attn_combine_tree(
+        _ptr(q), _ptr(k_ext), _ptr(v_ext), _ptr(qo_indptr), _ptr(kv_indptr), int(l_ext),
+        float(sm_scale), _ptr(custom_mask), _ptr(mask_indptr), _ptr(out), ctypes.byref(desc),
+        _ptr(workspace), workspace.numel(), _stream(stream))
+    _ok(rc, "verify_attn_combine_tree")
+    return out
+
+
+def append_desc(k, v, k_buf, v_buf) -> VaDesc:
+    """Descriptor for verify_attn_append_kv (only head counts, dims, dtype and
+    the four strides are read)."""
+    d = VaDesc()
+    d.bs = 1
+    d.h_q = k.shape[1]
+    d.h_kv = k.shape[1]
+    d.head_dim = k.shape[2]
+    d.v_head_dim = v.shape[2]
+    d.kv_dtype = _dtype_code(k_buf)
+    d.q_rows = k.shape[0]
+    d.num_kv_indices = 0
+    for field, t, name in (("kext_stride", k, "k"), ("vext_stride", v, "v"),
+                           ("kbuf_stride", k_buf, "k_buf"), ("vbuf_stride", v_buf, "v_buf")):
+        st = _strides(t, name)
+        getattr(d, field)[0], getattr(d, field)[1] = st[0], st[1]
+    return d
+
+
+def verify_attn_append_kv(k, v, out_cache_loc, k_buf, v_buf, k_scale=1.0, v_scale=1.0, stream=None):
+    """Write draft K/V rows into the pool at ``out_cache_loc`` (int64), casting
+    to E4M3FN (x / scale, saturating) when the pool is fp8."""
+    desc = append_desc(k, v, k_buf, v_buf)
+    n = int(out_cache_loc.numel())
+    rc = _lib.verify_attn_append_kv(_ptr(k) if n else 0, _ptr(v) if n else 0,
+                                    _ptr(out_cache_loc) if n else 0, n, float(k_scale), float(v_scale),
+                                    _ptr(k_buf), _ptr(v_buf), ctypes.byref(desc), _stream(stream))
+    _ok(rc, "verify_attn_append_kv")
+
+
+def verify_attn_build_kv_indices(req_to_token, req_pool_indices, seq_lens, kv_indptr, kv_indices,
+                                 kv_start_idx=None, stream=None):
+    """Fill ``kv_indptr`` (int32, bs + 1) and ``kv_indices`` (int64) from the
+    request-to-token table (int32 [rows, stride])."""
+    bs = int(seq_lens.numel())
+    rc = _lib.verify_attn_build_kv_indices(
+        _ptr(req_to_token), int(req_to_token.stride(0)), _ptr(req_pool_indices), _ptr(seq_lens),
+        _ptr(kv_start_idx) if kv_start_idx is not None else 0, bs, int(kv_indices.numel()),
+        _ptr(kv_indptr), _ptr(kv_indices) if kv_indices.numel() else 0, _stream(stream))
+    _ok(rc, "verify_attn_build_kv_indices")
 
 
 class VerifyAttn:

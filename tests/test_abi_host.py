@@ -29,7 +29,8 @@ def test_header_declares_the_documented_entry_points():
     names = set(declared_symbols())
     assert {"verify_attn_run", "verify_attn_prefix", "verify_attn_combine", "verify_attn_check",
             "verify_attn_plan", "verify_attn_workspace_bytes", "verify_attn_strerror",
-            "verify_attn_last_error", "verify_attn_version"} <= names
+            "verify_attn_last_error", "verify_attn_version", "verify_attn_run_tree",
+            "verify_attn_combine_tree", "verify_attn_append_kv", "verify_attn_build_kv_indices"} <= names
 
 
 def test_library_exports_every_declared_symbol():
@@ -141,3 +142,57 @@ def test_run_rejects_bad_arguments_without_launching():
                                   ctypes.c_float(0.1), ctypes.c_float(1.0), ctypes.c_float(1.0),
                                   None, ctypes.byref(d), None, 0, None)
     assert rc < 0
+
+
+# ---------------------------------------------- tree / append / index build ---
+def test_tree_entry_rejects_bad_mask_arguments():
+    lib = va.lib()
+    d = desc_of(l_ext=4)
+    fake = ctypes.c_void_p(256)  # never dereferenced: every call below fails validation first
+    args = lambda mask, mi, l_ext, dd: (fake, fake, fake, fake, fake, fake, fake, fake, l_ext,
+                                        ctypes.c_float(0.1), ctypes.c_float(1.0), ctypes.c_float(1.0),
+                                        mask, mi, fake, ctypes.byref(dd), fake, 1 << 30, None)
+    assert lib.verify_attn_run_tree(*args(None, fake, 4, d)) == -1
+    assert lib.verify_attn_run_tree(*args(fake, None, 4, d)) == -1
+    d65 = desc_of(l_ext=65)
+    assert lib.verify_attn_run_tree(*args(fake, fake, 65, d65)) == -6
+
+
+def _append_desc(kv_dtype=torch.bfloat16, d=128, h=2):
+    m = lambda *s, dt=torch.bfloat16: torch.empty(*s, dtype=dt, device="meta")
+    return va.append_desc(m(8, h, d), m(8, h, d), m(100, h, d, dt=kv_dtype), m(100, h, d, dt=kv_dtype))
+
+
+@pytest.mark.parametrize("mutate,n,scale,code", [
+    (lambda d: setattr(d, "kv_dtype", 9), 8, 1.0, -5),
+    (lambda d: setattr(d, "head_dim", 96), 8, 1.0, -4),
+    (lambda d: setattr(d, "h_kv", 0), 8, 1.0, -3),
+    (lambda d: d.kbuf_stride.__setitem__(0, 7), 8, 1.0, -7),
+    (lambda d: None, -1, 1.0, -13),
+])
+def test_append_rejects_bad_arguments(mutate, n, scale, code):
+    d = _append_desc()
+    mutate(d)
+    fake = ctypes.c_void_p(256)
+    rc = va.lib().verify_attn_append_kv(fake, fake, fake, n, ctypes.c_float(scale), ctypes.c_float(scale),
+                                        fake, fake, ctypes.byref(d), None)
+    assert rc == code
+
+
+def test_append_fp8_rejects_bad_scales_and_empty_is_a_no_op():
+    d = _append_desc(torch.float8_e4m3fn)
+    fake = ctypes.c_void_p(256)
+    lib = va.lib()
+    for ks in (0.0, -1.0, float("nan"), float("inf")):
+        assert lib.verify_attn_append_kv(fake, fake, fake, 8, ctypes.c_float(ks), ctypes.c_float(1.0),
+                                         fake, fake, ctypes.byref(d), None) == -8
+    assert lib.verify_attn_append_kv(None, None, None, 0, ctypes.c_float(1.0), ctypes.c_float(1.0),
+                                     None, None, ctypes.byref(d), None) == 0
+
+
+def test_build_kv_indices_rejects_bad_arguments():
+    lib = va.lib()
+    fake = ctypes.c_void_p(256)
+    assert lib.verify_attn_build_kv_indices(fake, 10, fake, fake, None, 0, 10, fake, fake, None) == -2
+    assert lib.verify_attn_build_kv_indices(fake, 10, fake, None, None, 2, 10, fake, fake, None) == -1
+    assert lib.verify_attn_build_kv_indices(fake, -1, fake, fake, None, 2, 10, fake, fake, None) == -13

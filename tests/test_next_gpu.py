@@ -1,0 +1,188 @@
+"""Parity of the paths around verify attention with the oracle, through the C
+ABI: the tree-masked draft block (topk > 1), the draft K/V append into the
+pool (bit-exact codes / bits) and the kv_indices build (bit-exact).
+Tolerances for the attention outputs are those of test_parity_gpu.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from speculative_decoding_attention_amd import workloads as W
+from test_oracle_pins_next import pack_masks, tree_mask
+from test_parity_gpu import BF16_TOL, FP8_TOL, assert_close, dev, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def va():
+    from speculative_decoding_attention_amd import verify_attn
+    return verify_attn
+
+
+def tree_case(p, seed):
+    gen = torch.Generator().manual_seed(seed)
+    dm = [tree_mask(p.l_ext, gen) for _ in range(p.bs)]
+    mask, mi = pack_masks(p, dm, gen)
+    return dm, mask, mi
+
+
+def run_tree(va, pg, mask, mi, **kw):
+    m = torch.from_numpy(mask).to(dev())
+    i = torch.from_numpy(mi).to(dev())
+    out = va.verify_attn_run_tree(pg.q, pg.k_ext, pg.v_ext, pg.k_buf, pg.v_buf, pg.qo_indptr,
+                                  pg.kv_indptr, pg.kv_indices, pg.l_ext, m, i, pg.sm_scale, pg.k_scale,
+                                  pg.v_scale, **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_tree(p, mask, mi):
+    return oracle.verify_attn(p.q, p.k_ext, p.v_ext, p.k_buf, p.v_buf, p.qo_indptr, p.kv_indptr,
+                              p.kv_indices, p.sm_scale, p.k_scale, p.v_scale, custom_mask=mask,
+                              mask_indptr=mi)
+
+
+# ------------------------------------------------------------------ tree mask ---
+@pytest.mark.parametrize("l_ext", [4, 8, 13])
+@pytest.mark.parametrize("kv_dtype", [torch.bfloat16, torch.float8_e4m3fn])
+def test_tree_mask_parity(va, l_ext, kv_dtype):
+    d = 256 if kv_dtype == torch.bfloat16 else 128
+    p = W.make_problem([700, 0, 1500, 33], l_ext, 8, 2, d, d, kv_dtype=kv_dtype, k_scale=0.5,
+                       v_scale=0.25, pool_factor=2, permute=True, seed=300 + l_ext,
+                       name="tree L=%d %s" % (l_ext, kv_dtype))
+    dm, mask, mi = tree_case(p, 7 + l_ext)
+    out = run_tree(va, p.to(dev()), mask, mi)
+    assert_close(out, oracle_tree(p, mask, mi), FP8_TOL if p.kv_fp8 else BF16_TOL, p.name)
+
+
+def test_causal_tree_mask_equals_causal_run(va):
+    p = W.make_problem([513, 64], 4, 16, 2, 256, 256, seed=311, name="causal via tree")
+    gen = torch.Generator().manual_seed(3)
+    mask, mi = pack_masks(p, [np.tril(np.ones((4, 4), np.uint8))] * p.bs, gen)
+    pg = p.to(dev())
+    a = run_tree(va, pg, mask, mi)
+    b = run_gpu(va, pg)
+    assert torch.equal(a, b)
+
+
+def test_tree_row_with_nothing_visible_is_zero(va):
+    p = W.make_problem([0, 40], 3, 4, 1, 64, 64, seed=312, name="empty row")
+    dm = [np.eye(3, dtype=np.uint8), np.eye(3, dtype=np.uint8)]
+    dm[0][2, 2] = 0
+    gen = torch.Generator().manual_seed(4)
+    mask, mi = pack_masks(p, dm, gen)
+    out = run_tree(va, p.to(dev()), mask, mi)
+    assert torch.count_nonzero(out[2].float()) == 0
+    assert_close(out, oracle_tree(p, mask, mi), BF16_TOL, p.name)
+
+
+def test_tree_headline_shape(va):
+    p = W.config_b8_8k()
+    dm, mask, mi = tree_case(p, 11)
+    out = run_tree(va, p.to(dev()), mask, mi)
+    assert_close(out, oracle_tree(p, mask, mi), BF16_TOL, "tree b8_8k")
+
+
+# -------------------------------------------------------------------- append ---
+def append_case(kv_dtype, n, h_kv, d, pool, seed, scale_k=0.03125, scale_v=0.0625):
+    g = torch.Generator().manual_seed(seed)
+    k = (torch.randn(n, h_kv, d, generator=g) * 3).to(torch.bfloat16)
+    v = (torch.randn(n, h_kv, d, generator=g) * 3).to(torch.bfloat16)
+    loc = torch.randperm(pool, generator=g)[:n].to(torch.int64)
+    kb = torch.randn(pool, h_kv, d, generator=g).to(kv_dtype)
+    vb = torch.randn(pool, h_kv, d, generator=g).to(kv_dtype)
+    return k, v, loc, kb, vb, scale_k, scale_v
+
+
+def bits(t):
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8).cpu().numpy()
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("kv_dtype", [torch.bfloat16, torch.float8_e4m3fn])
+def test_append_bit_exact(va, kv_dtype, d):
+    k, v, loc, kb, vb, ks, vs = append_case(kv_dtype, 300, 2, d, 1000, seed=d)
+    # include grid midpoints and values past 448 after the division
+    k[0, 0, :8] = torch.tensor([1.0625, 1.1875, 0.53125, 3 * 2.0 ** -10, 460.0, 464.0, 500.0, -1e4]
+                               ).mul(ks).to(torch.bfloat16)
+    ek, ev = oracle.append_kv(k, v, loc, kb, vb, ks, vs)
+    kg, vg, lg = k.to(dev()), v.to(dev()), loc.to(dev())
+    kbg, vbg = kb.to(dev()), vb.to(dev())
+    va.verify_attn_append_kv(kg, vg, lg, kbg, vbg, ks, vs)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(kbg), ek)
+    np.testing.assert_array_equal(bits(vbg), ev)
+
+
+def test_append_strided_views_and_empty(va):
+    k, v, loc, kb, vb, ks, vs = append_case(torch.float8_e4m3fn, 64, 4, 128, 200, seed=5)
+    # k/v as head slices of a wider tensor; the pool as a view of a wider pool
+    kw = torch.zeros(64, 8, 128, dtype=torch.bfloat16)
+    kw[:, 2:6] = k
+    kpool = torch.zeros(200, 6, 128, dtype=torch.float8_e4m3fn)
+    kpool[:, 1:5] = kb
+    ek, ev = oracle.append_kv(k, v, loc, kb, vb, ks, vs)
+    kwg, vg, lg = kw.to(dev()), v.to(dev()), loc.to(dev())
+    kpg, vbg = kpool.to(dev()), vb.to(dev())
+    va.verify_attn_append_kv(kwg[:, 2:6], vg, lg, kpg[:, 1:5], vbg, ks, vs)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(kpg[:, 1:5].contiguous()), ek)
+    np.testing.assert_array_equal(bits(vbg), ev)
+    assert torch.count_nonzero(kpg[:, 0].view(torch.uint8)) == 0  # neighbouring head untouched
+    before = vbg.clone()
+    va.verify_attn_append_kv(vg[:0], vg[:0], lg[:0], vbg, vbg, ks, vs)
+    torch.cuda.synchronize()
+    assert torch.equal(before.view(torch.uint8), vbg.view(torch.uint8))
+
+
+def test_append_then_verify_sees_the_new_rows(va):
+    # the step before verify: drafts written into the pool become prefix rows
+    # of the next step; verify over them matches the oracle on the pool the
+    # oracle's own append produced
+    p = W.make_problem([300, 200], 4, 8, 1, 128, 128, kv_dtype=torch.float8_e4m3fn, seed=321,
+                       pool_factor=2, permute=True, name="append+verify")
+    free = torch.tensor(sorted(set(range(p.k_buf.shape[0])) - set(p.kv_indices.tolist())))[:8]
+    ek, ev = oracle.append_kv(p.k_ext, p.v_ext, free, p.k_buf, p.v_buf, p.k_scale, p.v_scale)
+    pg = p.to(dev())
+    va.verify_attn_append_kv(pg.k_ext, pg.v_ext, free.to(dev()), pg.k_buf, pg.v_buf, p.k_scale, p.v_scale)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(pg.k_buf), ek)
+    np.testing.assert_array_equal(bits(pg.v_buf), ev)
+
+
+# --------------------------------------------------------- kv_indices build ---
+@pytest.mark.parametrize("with_start", [False, True])
+def test_build_kv_indices_bit_exact(va, with_start):
+    g = torch.Generator().manual_seed(17)
+    rows, stride, bs = 40, 70000, 6
+    rt = torch.randint(0, 1 << 30, (rows, stride), generator=g, dtype=torch.int32)
+    rp = torch.randperm(rows, generator=g)[:bs].to(torch.int64)
+    sl = torch.tensor([0, 17, 65000, 1, 4096, 300], dtype=torch.int32)
+    st = torch.tensor([3, 0, 20, 69000, 5, 9], dtype=torch.int32) if with_start else None
+    eptr, eidx = oracle.build_kv_indices(rt, rp, sl, st)
+    total = int(sl.sum())
+    kvp = torch.full((bs + 1,), -7, dtype=torch.int32, device=dev())
+    kvi = torch.full((total + 5,), -7, dtype=torch.int64, device=dev())
+    va.verify_attn_build_kv_indices(rt.to(dev()), rp.to(dev()), sl.to(dev()), kvp, kvi[:total],
+                                    None if st is None else st.to(dev()))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(kvp.cpu().numpy(), eptr)
+    np.testing.assert_array_equal(kvi[:total].cpu().numpy(), eidx)
+    assert (kvi[total:].cpu() == -7).all()  # nothing written past the capacity
+
+
+def test_build_kv_indices_respects_capacity(va):
+    rt = torch.arange(1000, dtype=torch.int32).view(1, 1000)
+    rp = torch.zeros(1, dtype=torch.int64)
+    sl = torch.tensor([900], dtype=torch.int32)
+    kvp = torch.zeros(2, dtype=torch.int32, device=dev())
+    kvi = torch.full((1000,), -1, dtype=torch.int64, device=dev())
+    va.verify_attn_build_kv_indices(rt.to(dev()), rp.to(dev()), sl.to(dev()), kvp, kvi[:100])
+    torch.cuda.synchronize()
+    assert kvi[:100].cpu().tolist() == list(range(100))
+    assert (kvi[100:].cpu() == -1).all()
+    assert kvp.cpu().tolist() == [0, 900]
