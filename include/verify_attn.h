@@ -177,6 +177,34 @@ VA_API int verify_attn_combine(const void *q, const void *k_ext, const void *v_e
                                const va_desc_t *desc, void *workspace, size_t workspace_bytes,
                                void *stream);
 
+/* Page-table prefix (page_size > 1; the unified-verify block table of sglang's
+ * aiter_backend.py, which views the pool as [pages, page_size, H_KV, D]): as
+ * verify_attn_run / verify_attn_prefix, but the prefix rows come from
+ * block_table (int32, row b at block_table + b * block_table_stride) instead
+ * of kv_indices: token t < n_b of sequence b is pool row
+ *   block_table[b * block_table_stride + t / page_size] * page_size
+ *     + t % page_size
+ * of k_buf / v_buf (whose desc strides are per token row).  kv_indptr still
+ * gives the prefix lengths n_b = kv_indptr[b+1] - kv_indptr[b], and
+ * desc->num_kv_indices their host-known total.  page_size >= 1; page ids and
+ * table bounds are not checked (device data). */
+VA_API int verify_attn_run_paged(const void *q, const void *k_ext, const void *v_ext,
+                                 const void *k_buf, const void *v_buf,
+                                 const int32_t *qo_indptr, const int32_t *kv_indptr,
+                                 const int32_t *block_table, int64_t block_table_stride,
+                                 int32_t page_size, int32_t l_ext,
+                                 float sm_scale, float k_scale, float v_scale, void *out,
+                                 const va_desc_t *desc, void *workspace, size_t workspace_bytes,
+                                 void *stream);
+
+VA_API int verify_attn_prefix_paged(const void *q, const void *k_buf, const void *v_buf,
+                                    const int32_t *qo_indptr, const int32_t *kv_indptr,
+                                    const int32_t *block_table, int64_t block_table_stride,
+                                    int32_t page_size, int32_t l_ext,
+                                    float sm_scale, float k_scale, float v_scale,
+                                    const va_desc_t *desc, void *workspace, size_t workspace_bytes,
+                                    void *stream);
+
 /* Tree verify (topk > 1): as verify_attn_run / verify_attn_combine, but the
  * draft block follows a tree mask instead of the causal rule.  Layout of the
  * mask as sglang's aiter_backend.py builds it for extend attention with

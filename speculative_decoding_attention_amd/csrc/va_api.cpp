@@ -67,11 +67,15 @@ int check_workspace(const va_plan_t &plan, const void *ws, size_t ws_bytes)
 int prefix_impl(const void *q, const void *k_buf, const void *v_buf, const int32_t *qo_indptr,
                 const int32_t *kv_indptr, const int64_t *kv_indices, int32_t l_ext, float sm_scale,
                 float k_scale, float v_scale, const va_desc_t *desc, const va_plan_t &plan,
-                void *workspace, void *stream)
+                void *workspace, void *stream, const int32_t *block_table = nullptr,
+                int64_t bt_stride = 0, int32_t page_size = 1)
 {
     if (plan.prefix_blocks == 0)
         return VA_OK;  // no prefix token anywhere: the combine pass sees zero ranges
     PrefixParams p;
+    p.block_table = block_table;
+    p.bt_s0 = bt_stride;
+    p.page_size = page_size;
     p.q = (const uint16_t *)q;
     p.k_buf = (const uint8_t *)k_buf;
     p.v_buf = (const uint8_t *)v_buf;
@@ -145,6 +149,24 @@ int combine_impl(const void *q, const void *k_ext, const void *v_ext, const int3
     if (e != 0) {
         set_error("combine kernel launch: %s", hip_error_string(e));
         return VA_ERR_DEVICE;
+    }
+    return VA_OK;
+}
+
+// Page-table arguments of the *_paged entry points.
+int check_paged(const va_desc_t *desc, const int32_t *block_table, int64_t bt_stride, int32_t page_size)
+{
+    if (page_size < 1) {
+        set_error("page_size = %d; need >= 1", page_size);
+        return VA_ERR_SIZE;
+    }
+    if (bt_stride < 0) {
+        set_error("block table stride %lld is negative", (long long)bt_stride);
+        return VA_ERR_STRIDE;
+    }
+    if (desc->num_kv_indices > 0 && !block_table) {
+        set_error("block_table is NULL");
+        return VA_ERR_NULL_ARG;
     }
     return VA_OK;
 }
@@ -312,6 +334,69 @@ VA_API int verify_attn_run_tree(const void *q, const void *k_ext, const void *v_
         return rc;
     return va::combine_impl(q, k_ext, v_ext, qo_indptr, kv_indptr, l_ext, sm_scale, out, desc, plan,
                             workspace, stream, custom_mask, mask_indptr);
+}
+
+VA_API int verify_attn_prefix_paged(const void *q, const void *k_buf, const void *v_buf,
+                                    const int32_t *qo_indptr, const int32_t *kv_indptr,
+                                    const int32_t *block_table, int64_t block_table_stride,
+                                    int32_t page_size, int32_t l_ext, float sm_scale, float k_scale,
+                                    float v_scale, const va_desc_t *desc, void *workspace,
+                                    size_t workspace_bytes, void *stream)
+{
+    int rc = va::check_desc(desc, l_ext);
+    if (rc != VA_OK)
+        return rc;
+    const void *ptrs[5] = {q, k_buf, v_buf, qo_indptr, kv_indptr};
+    if ((rc = va::check_ptrs(ptrs, 5)) != VA_OK)
+        return rc;
+    if ((rc = va::check_paged(desc, block_table, block_table_stride, page_size)) != VA_OK)
+        return rc;
+    const void *al[3] = {q, k_buf, v_buf};
+    if ((rc = va::check_align(al, 3)) != VA_OK)
+        return rc;
+    if ((rc = va::check_scales(sm_scale, k_scale, v_scale)) != VA_OK)
+        return rc;
+    va_plan_t plan;
+    if ((rc = va::make_plan(desc, l_ext, 0, &plan)) != VA_OK)
+        return rc;
+    if ((rc = va::check_workspace(plan, workspace, workspace_bytes)) != VA_OK)
+        return rc;
+    return va::prefix_impl(q, k_buf, v_buf, qo_indptr, kv_indptr, nullptr, l_ext, sm_scale, k_scale,
+                           v_scale, desc, plan, workspace, stream, block_table, block_table_stride,
+                           page_size);
+}
+
+VA_API int verify_attn_run_paged(const void *q, const void *k_ext, const void *v_ext, const void *k_buf,
+                                 const void *v_buf, const int32_t *qo_indptr, const int32_t *kv_indptr,
+                                 const int32_t *block_table, int64_t block_table_stride, int32_t page_size,
+                                 int32_t l_ext, float sm_scale, float k_scale, float v_scale, void *out,
+                                 const va_desc_t *desc, void *workspace, size_t workspace_bytes,
+                                 void *stream)
+{
+    int rc = va::check_desc(desc, l_ext);
+    if (rc != VA_OK)
+        return rc;
+    const void *ptrs[8] = {q, k_ext, v_ext, k_buf, v_buf, qo_indptr, kv_indptr, out};
+    if ((rc = va::check_ptrs(ptrs, 8)) != VA_OK)
+        return rc;
+    if ((rc = va::check_paged(desc, block_table, block_table_stride, page_size)) != VA_OK)
+        return rc;
+    const void *al[6] = {q, k_ext, v_ext, k_buf, v_buf, out};
+    if ((rc = va::check_align(al, 6)) != VA_OK)
+        return rc;
+    if ((rc = va::check_scales(sm_scale, k_scale, v_scale)) != VA_OK)
+        return rc;
+    va_plan_t plan;
+    if ((rc = va::make_plan(desc, l_ext, 0, &plan)) != VA_OK)
+        return rc;
+    if ((rc = va::check_workspace(plan, workspace, workspace_bytes)) != VA_OK)
+        return rc;
+    rc = va::prefix_impl(q, k_buf, v_buf, qo_indptr, kv_indptr, nullptr, l_ext, sm_scale, k_scale, v_scale,
+                         desc, plan, workspace, stream, block_table, block_table_stride, page_size);
+    if (rc != VA_OK)
+        return rc;
+    return va::combine_impl(q, k_ext, v_ext, qo_indptr, kv_indptr, l_ext, sm_scale, out, desc, plan,
+                            workspace, stream);
 }
 
 }  // extern "C"

@@ -49,6 +49,11 @@ struct PrefixParams {
     const int32_t *qo_indptr;
     const int32_t *kv_indptr;
     const int64_t *kv_indices;
+    // page-table prefix (NULL: kv_indices): token t of sequence b is pool row
+    // block_table[b * bt_s0 + t / page_size] * page_size + t % page_size
+    const int32_t *block_table;
+    int64_t bt_s0;
+    int32_t page_size;
     uint16_t *part_o;  // [range_slots * h_kv, rows, D] bf16 (round to nearest even)
     float *part_lse;   // [range_slots * h_kv, rows]    fp32 (natural log)
     int64_t q_s0, q_s1;        // elements

@@ -409,7 +409,12 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64) void prefix_kernel(
         if (lane < 2 * RW) {
             int tok = k * TN + wave * RW + (lane >> 1);
             tok = tok < len ? tok : len - 1;
-            const uint32_t *src = (const uint32_t *)(p.kv_indices + kv0 + tok) + (lane & 1);
+            // token rows: the two dwords of the int64 index; page table: both
+            // lanes of the pair fetch the token's page id
+            const uint32_t *src =
+                p.block_table
+                    ? (const uint32_t *)(p.block_table + (int64_t)rg.b * p.bt_s0 + (rg.start + tok) / p.page_size)
+                    : (const uint32_t *)(p.kv_indices + kv0 + tok) + (lane & 1);
             dma4(src, __builtin_amdgcn_readfirstlane(idx_base + (k % G::NIDX) * RW * 8));
         }
     };
@@ -424,7 +429,12 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64) void prefix_kernel(
             const int row = wave * RW + rl;           // row within the tile
             const int pc = lane % LCH;                // LDS chunk within the row
             const int vz = vswz(row);
-            const uint64_t t = (uint64_t)ix[rl];
+            uint64_t t = (uint64_t)ix[rl];
+            if (p.block_table) {  // pool row = page id * page_size + position in the page
+                int tok = k * TN + row;
+                tok = tok < len ? tok : len - 1;
+                t = (uint64_t)(uint32_t)t * (uint32_t)p.page_size + (uint32_t)((rg.start + tok) % p.page_size);
+            }
             dma16(kbase + t * p.kb_s0 + ((pc ^ kswz(row)) << 4),
                   __builtin_amdgcn_readfirstlane(st + i * 1024));
             dma16(vbase + t * p.vb_s0 + ((pc ^ vz) << 4),

@@ -68,6 +68,9 @@ def _load():
     lib.verify_attn_run.argtypes = [P, P, P, P, P, P, P, P, I32, F, F, F, P, DP, P, SZ, P]
     lib.verify_attn_prefix.argtypes = [P, P, P, P, P, P, I32, F, F, F, DP, P, SZ, P]
     lib.verify_attn_combine.argtypes = [P, P, P, P, P, I32, F, P, DP, P, SZ, P]
+    lib.verify_attn_run_paged.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_int64, I32, I32, F, F, F, P, DP,
+                                          P, SZ, P]
+    lib.verify_attn_prefix_paged.argtypes = [P, P, P, P, P, P, ctypes.c_int64, I32, I32, F, F, F, DP, P, SZ, P]
     lib.verify_attn_run_tree.argtypes = [P, P, P, P, P, P, P, P, I32, F, F, F, P, P, P, DP, P, SZ, P]
     lib.verify_attn_combine_tree.argtypes = [P, P, P, P, P, I32, F, P, P, P, DP, P, SZ, P]
     lib.verify_attn_append_kv.argtypes = [P, P, P, ctypes.c_int64, F, F, P, P, DP, P]
@@ -75,6 +78,7 @@ def _load():
     for name in ("verify_attn_check", "verify_attn_plan", "verify_attn_workspace_bytes",
                  "verify_attn_run", "verify_attn_prefix", "verify_attn_combine",
                  "verify_attn_run_tree", "verify_attn_combine_tree", "verify_attn_append_kv",
+                 "verify_attn_run_paged", "verify_attn_prefix_paged",
                  "verify_attn_build_kv_indices",
                  "verify_attn_version"):
         getattr(lib, name).restype = ctypes.c_int
@@ -224,6 +228,33 @@ def verify_attn_combine(q, k_ext, v_ext, qo_indptr, kv_indptr, l_ext, sm_scale, 
         float(sm_scale), _ptr(out), ctypes.byref(desc), _ptr(workspace), workspace.numel(),
         _stream(stream))
     _ok(rc, "verify_attn_combine")
+    return out
+
+
+def verify_attn_run_paged(q, k_ext, v_ext, k_buf, v_buf, qo_indptr, kv_indptr, block_table, page_size,
+                          l_ext, num_prefix_tokens, sm_scale=None, k_scale=1.0, v_scale=1.0, out=None,
+                          workspace=None, split_tokens=0, n_splits=0, stream=None, desc=None):
+    """Verify over a page-table prefix: token t of sequence b is pool row
+    ``block_table[b, t // page_size] * page_size + t % page_size``
+    (``block_table`` int32 [bs, max_pages]); ``num_prefix_tokens`` is the
+    host-known total of the prefix lengths."""
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(q.shape[2])
+    if out is None:
+        out = torch.empty(q.shape[0], q.shape[1], v_ext.shape[2], dtype=q.dtype, device=q.device)
+    bs = qo_indptr.shape[0] - 1
+    if desc is None:
+        desc = make_desc(q, k_ext, v_ext, k_buf, v_buf,
+                         torch.empty(int(num_prefix_tokens), dtype=torch.int64, device="meta"),
+                         out, bs, split_tokens, n_splits)
+    if workspace is None:
+        workspace = alloc_workspace(desc, l_ext, q.device)
+    rc = _lib.verify_attn_run_paged(
+        _ptr(q), _ptr(k_ext), _ptr(v_ext), _ptr(k_buf), _ptr(v_buf), _ptr(qo_indptr), _ptr(kv_indptr),
+        _ptr(block_table), int(block_table.stride(0)), int(page_size), int(l_ext), float(sm_scale),
+        float(k_scale), float(v_scale), _ptr(out), ctypes.byref(desc), _ptr(workspace), workspace.numel(),
+        _stream(stream))
+    _ok(rc, "verify_attn_run_paged")
     return out
 
 

@@ -157,6 +157,26 @@ def make_problem(prefix_lens, l_ext, h_q, h_kv, head_dim, v_head_dim=None, *,
                    float(v_scale), prefix_lens)
 
 
+def make_paged_block_table(prefix_lens, page_size, pages, seed=0, device="cpu"):
+    """Seeded page table for a pool of ``pages`` pages of ``page_size`` token
+    rows: int32 [bs, max_pages], each sequence drawing distinct random page
+    ids for its ceil(n_b / page_size) pages (unused entries 0).  A generator
+    only: which pool row a token lands in is left to the code under test."""
+    prefix_lens = [int(n) for n in prefix_lens]
+    need = [(n + page_size - 1) // page_size for n in prefix_lens]
+    if sum(need) > pages:
+        raise ValueError("pool of %d pages too small for %d" % (pages, sum(need)))
+    g = torch.Generator().manual_seed(seed)
+    perm = torch.randperm(pages, generator=g)
+    width = max(1, max(need))
+    table = torch.zeros(len(prefix_lens), width, dtype=torch.int32)
+    pos = 0
+    for b, k in enumerate(need):
+        table[b, :k] = perm[pos:pos + k].to(torch.int32)
+        pos += k
+    return table.to(device)
+
+
 # The five workloads the path is specified on.  "tiny" finishes in the oracle
 # in milliseconds; "b8_8k" is the headline throughput workload.
 def config_tiny(device="cpu", seed=1):

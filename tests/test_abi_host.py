@@ -196,3 +196,15 @@ def test_build_kv_indices_rejects_bad_arguments():
     assert lib.verify_attn_build_kv_indices(fake, 10, fake, fake, None, 0, 10, fake, fake, None) == -2
     assert lib.verify_attn_build_kv_indices(fake, 10, fake, None, None, 2, 10, fake, fake, None) == -1
     assert lib.verify_attn_build_kv_indices(fake, -1, fake, fake, None, 2, 10, fake, fake, None) == -13
+
+
+def test_paged_entry_rejects_bad_arguments():
+    lib = va.lib()
+    d = desc_of()
+    fake = ctypes.c_void_p(256)
+    call = lambda bt, stride, ps: lib.verify_attn_run_paged(
+        fake, fake, fake, fake, fake, fake, fake, bt, stride, ps, 4, ctypes.c_float(0.1),
+        ctypes.c_float(1.0), ctypes.c_float(1.0), fake, ctypes.byref(d), fake, 1 << 30, None)
+    assert call(fake, 8, 0) == -13
+    assert call(fake, -1, 16) == -7
+    assert call(None, 8, 16) == -1

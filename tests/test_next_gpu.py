@@ -186,3 +186,58 @@ def test_build_kv_indices_respects_capacity(va):
     assert kvi[:100].cpu().tolist() == list(range(100))
     assert (kvi[100:].cpu() == -1).all()
     assert kvp.cpu().tolist() == [0, 900]
+
+
+# ------------------------------------------------------ page-table prefix ---
+def paged_case(lens, page_size, l_ext, h_q, h_kv, d, kv_dtype, seed):
+    """A problem whose pool holds 2x the needed pages; the page table is the
+    prefix's address; kv_indices is the oracle's expansion of it."""
+    pages = 2 * sum((n + page_size - 1) // page_size for n in lens) + 1
+    p = W.make_problem(lens, l_ext, h_q, h_kv, d, d, kv_dtype=kv_dtype, k_scale=0.5, v_scale=0.25,
+                       pool_factor=None, seed=seed, name="paged P=%d" % page_size)
+    # a pool of pages * page_size token rows with fresh seeded contents
+    g = torch.Generator().manual_seed(seed + 1)
+    rows = pages * page_size
+    if kv_dtype == torch.float8_e4m3fn:
+        p.k_buf = torch.randn(rows, h_kv, d, generator=g).mul(30).to(kv_dtype)
+        p.v_buf = torch.randn(rows, h_kv, d, generator=g).mul(30).to(kv_dtype)
+    else:
+        p.k_buf = torch.randn(rows, h_kv, d, generator=g).to(kv_dtype)
+        p.v_buf = torch.randn(rows, h_kv, d, generator=g).to(kv_dtype)
+    table = W.make_paged_block_table(lens, page_size, pages, seed=seed)
+    p.kv_indices = torch.from_numpy(oracle.expand_block_table(table, p.kv_indptr, page_size))
+    return p, table
+
+
+@pytest.mark.parametrize("page_size", [1, 16, 64])
+@pytest.mark.parametrize("kv_dtype", [torch.bfloat16, torch.float8_e4m3fn])
+def test_paged_prefix_parity(va, page_size, kv_dtype):
+    d = 256 if kv_dtype == torch.bfloat16 else 128
+    p, table = paged_case([1000, 0, 37, 2049], page_size, 4, 8, 2, d, kv_dtype, seed=400 + page_size)
+    pg = p.to(dev())
+    out = va.verify_attn_run_paged(pg.q, pg.k_ext, pg.v_ext, pg.k_buf, pg.v_buf, pg.qo_indptr, pg.kv_indptr,
+                                   table.to(dev()), page_size, p.l_ext, sum(p.prefix_lens), p.sm_scale,
+                                   p.k_scale, p.v_scale)
+    torch.cuda.synchronize()
+    ref = oracle.verify_attn(p.q, p.k_ext, p.v_ext, p.k_buf, p.v_buf, p.qo_indptr, p.kv_indptr,
+                             p.kv_indices, p.sm_scale, p.k_scale, p.v_scale)
+    assert_close(out, ref, FP8_TOL if p.kv_fp8 else BF16_TOL, p.name)
+    # the same rows through kv_indices give the same bits
+    assert torch.equal(out, run_gpu(va, pg))
+
+
+def test_paged_headline_shape(va):
+    p, table = paged_case([8192] * 8, 16, 4, 16, 2, 256, torch.bfloat16, seed=410)
+    pg = p.to(dev())
+    out = va.verify_attn_run_paged(pg.q, pg.k_ext, pg.v_ext, pg.k_buf, pg.v_buf, pg.qo_indptr, pg.kv_indptr,
+                                   table.to(dev()), 16, p.l_ext, sum(p.prefix_lens), p.sm_scale,
+                                   p.k_scale, p.v_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out, run_gpu(va, pg))
+    sel = [(b, h) for b in (0, 7) for h in (0, 15)]
+    ref = oracle.verify_attn(p.q, p.k_ext, p.v_ext, p.k_buf, p.v_buf, p.qo_indptr, p.kv_indptr,
+                             p.kv_indices, p.sm_scale, p.k_scale, p.v_scale, select=sel)
+    rows = np.zeros(out.shape, dtype=bool)
+    for b, h in sel:
+        rows[b * 4:(b + 1) * 4, h] = True
+    assert_close(out, ref, BF16_TOL, "paged b8_8k sampled", mask=rows)
