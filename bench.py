@@ -47,8 +47,10 @@ def parse_args():
 
 
 def kernel_source_hash():
+    """Hash of what decides the prefix kernel's traffic: its source, its
+    parameter header and the split planner (argument marshalling excluded)."""
     h = hashlib.sha256()
-    for name in ("va_kernels.hip", "va_internal.h", "va_api.cpp", "va_plan.cpp"):
+    for name in ("va_kernels.hip", "va_internal.h", "va_plan.cpp"):
         with open(os.path.join(ROOT, "speculative_decoding_attention_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -237,6 +239,104 @@ def calibration_copy(torch):
     del src, dst
 
 
+def _time_calls(torch, fn, steps, warmup):
+    """Mean µs of fn(i) over `steps` calls enqueued behind a GPU hold, events
+    on the current stream."""
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    hold_gpu(torch)
+    e0.record(stream)
+    for i in range(steps):
+        fn(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / steps
+
+
+def time_extensions(torch, va, W, steps, replicas):
+    """The paths around verify: tree-masked verify and page-table verify on
+    the headline shape (cold, rotating replicas), the draft K/V append and the
+    kv_indices build.  Returns a dict of µs and GB/s."""
+    import numpy as np
+    dev = torch.device("cuda", 0)
+    res = {}
+    probs = [W.config_b8_8k(device=dev, seed=3000 + r) for r in range(replicas)]
+    p0 = probs[0]
+    out = torch.empty(p0.q.shape[0], p0.h_q, p0.v_head_dim, dtype=torch.bfloat16, device=dev)
+    desc = va.make_desc(p0.q, p0.k_ext, p0.v_ext, p0.k_buf, p0.v_buf, p0.kv_indices, out, p0.bs)
+    ws = va.alloc_workspace(desc, p0.l_ext, dev)
+    kvb = p0.kv_bytes()
+
+    # tree verify: random draft trees (each node sees its ancestors)
+    g = torch.Generator().manual_seed(1)
+    L, n = p0.l_ext, p0.prefix_lens[0]
+    parts, indptr = [], [0]
+    for b in range(p0.bs):
+        parent = [-1] + [int(torch.randint(-1, i, (1,), generator=g)) for i in range(1, L)]
+        m = np.ones((L, n + L), np.uint8)
+        m[:, n:] = 0
+        for i in range(L):
+            j = i
+            while j >= 0:
+                m[i, n + j] = 1
+                j = parent[j]
+        parts.append(m.reshape(-1))
+        indptr.append(indptr[-1] + m.size)
+    mask = torch.from_numpy(np.concatenate(parts)).to(dev)
+    mi = torch.tensor(indptr, dtype=torch.int64, device=dev)
+    us = _time_calls(torch, lambda i: va.verify_attn_run_tree(
+        *(lambda p: (p.q, p.k_ext, p.v_ext, p.k_buf, p.v_buf, p.qo_indptr, p.kv_indptr, p.kv_indices,
+                     p.l_ext, mask, mi, p.sm_scale, p.k_scale, p.v_scale))(probs[i % replicas]),
+        out=out, workspace=ws, desc=desc), steps, 5)
+    res["tree_verify_b8_8k"] = {"us_per_call": round(us, 3), "gbs": round(kvb / us / 1e3, 2)}
+
+    # page-table verify, 16-token pages over the same pool rows count
+    P = 16
+    pages = 2 * p0.bs * n // P
+    tables = [W.make_paged_block_table(p.prefix_lens, P, pages, seed=10 + r, device=dev)
+              for r, p in enumerate(probs)]
+    us = _time_calls(torch, lambda i: va.verify_attn_run_paged(
+        *(lambda p, t: (p.q, p.k_ext, p.v_ext, p.k_buf, p.v_buf, p.qo_indptr, p.kv_indptr, t, P, p.l_ext,
+                        sum(p.prefix_lens), p.sm_scale, p.k_scale, p.v_scale))(probs[i % replicas],
+                                                                              tables[i % replicas]),
+        out=out, workspace=ws, desc=desc), steps, 5)
+    res["paged16_verify_b8_8k"] = {"us_per_call": round(us, 3), "gbs": round(kvb / us / 1e3, 2)}
+    del probs, tables
+    torch.cuda.empty_cache()
+
+    # draft K/V append: the headline's draft rows, and a bulk append
+    for tag, ntok, kv_dtype in (("append_fp8_32tok", 32, torch.float8_e4m3fn),
+                                ("append_fp8_64k", 65536, torch.float8_e4m3fn),
+                                ("append_bf16_64k", 65536, torch.bfloat16)):
+        pool = 2 * ntok
+        k = torch.randn(ntok, 2, 256, device=dev).to(torch.bfloat16)
+        v = torch.randn(ntok, 2, 256, device=dev).to(torch.bfloat16)
+        loc = torch.randperm(pool, device=dev)[:ntok]
+        kb = torch.zeros(pool, 2, 256, device=dev).to(kv_dtype)
+        vb = torch.zeros(pool, 2, 256, device=dev).to(kv_dtype)
+        us = _time_calls(torch, lambda i: va.verify_attn_append_kv(k, v, loc, kb, vb, 0.05, 0.05), steps, 5)
+        eb = 1 if kv_dtype == torch.float8_e4m3fn else 2
+        moved = ntok * 2 * 512 * (2 + eb) + ntok * 8
+        res[tag] = {"us_per_call": round(us, 3), "gbs": round(moved / us / 1e3, 2), "bytes": moved}
+        del k, v, loc, kb, vb
+
+    # kv_indices build for the headline batch (8 x 8192 tokens)
+    bs, n = 8, 8192
+    rt = torch.randint(0, 1 << 30, (64, 16384), dtype=torch.int32, device=dev)
+    rp = torch.randperm(64, device=dev)[:bs]
+    sl = torch.full((bs,), n, dtype=torch.int32, device=dev)
+    kvp = torch.empty(bs + 1, dtype=torch.int32, device=dev)
+    kvi = torch.empty(bs * n, dtype=torch.int64, device=dev)
+    us = _time_calls(torch, lambda i: va.verify_attn_build_kv_indices(rt, rp, sl, kvp, kvi), steps, 5)
+    moved = bs * n * (4 + 8)
+    res["build_kv_indices_b8_8k"] = {"us_per_call": round(us, 3), "gbs": round(moved / us / 1e3, 2),
+                                     "bytes": moved}
+    return res
+
+
 def cpu_baseline(torch, W, p_dev, min_seconds=10.0, max_passes=8):
     """The fp64 oracle on the host cores over the whole headline batch."""
     import oracle
@@ -283,7 +383,7 @@ def main():
 
     secondary = {}
     if not args.quick:
-        for name, reps in (("b4_64k", 1), ("fp8_ragged", 8)):
+        for name, reps in (("b4_64k", 1), ("fp8_ragged", 8), ("decode_b64", 2), ("draft_extend_b16", 8)):
             r = time_workload(torch, va, W, name, max(20, args.steps // 4), 5, reps, seed0=2000)
             secondary[name] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in r.items()
                                if k not in ("problem", "name")}
@@ -292,6 +392,12 @@ def main():
                   file=sys.stderr, flush=True)
             del r
             torch.cuda.empty_cache()
+
+    extensions = {}
+    if not args.quick:
+        extensions = time_extensions(torch, va, W, max(20, args.steps // 4), args.replicas)
+        print("[bench] around verify: %s" % json.dumps(extensions), file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
 
     cpu = None
     if not (args.quick or args.no_cpu_baseline):
@@ -346,6 +452,7 @@ def main():
             "graph_replay": {"us_per_call": head["us_step_graph"],
                              "gbs": round(head["gbs_graph"], 2) if head["gbs_graph"] else None},
             "secondary": secondary,
+            "around_verify": extensions,
         },
     }
     print(json.dumps(line), flush=True)

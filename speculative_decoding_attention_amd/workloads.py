@@ -213,10 +213,28 @@ def config_b4_64k(device="cpu", seed=5):
                         seed=seed, device=device, name="b4_64k")
 
 
+# Reuse of the same entry point for other modes with a fixed extend length
+# per request: plain decode (l_ext = 1) of a large batch, and the draft model's
+# DRAFT_EXTEND_V2 step (num_draft_tokens new tokens per request over the
+# draft-side prefix); both with the headline attention geometry (16/2 heads,
+# D = 256, scattered pool) and seeded ragged prefixes.
+def config_decode_b64(device="cpu", seed=6):
+    return make_problem(fp8_prefix_lens(seed, bs=64, lo=2048, hi=6144), 1, 16, 2, 256, 256,
+                        pool_factor=2, permute=True, seed=seed, device=device, name="decode_b64")
+
+
+def config_draft_extend_b16(device="cpu", seed=7):
+    return make_problem(fp8_prefix_lens(seed, bs=16, lo=1024, hi=8192), 4, 16, 2, 256, 256,
+                        pool_factor=2, permute=True, seed=seed, device=device,
+                        name="draft_extend_b16")
+
+
 CONFIGS = {
     "tiny": config_tiny,
     "b3_512": config_b3_512,
     "b8_8k": config_b8_8k,
     "fp8_ragged": config_fp8_ragged,
     "b4_64k": config_b4_64k,
+    "decode_b64": config_decode_b64,
+    "draft_extend_b16": config_draft_extend_b16,
 }

@@ -241,3 +241,29 @@ def test_paged_headline_shape(va):
     for b, h in sel:
         rows[b * 4:(b + 1) * 4, h] = True
     assert_close(out, ref, BF16_TOL, "paged b8_8k sampled", mask=rows)
+
+
+# ---------------------------------------------- decode and draft-extend reuse ---
+@pytest.mark.parametrize("name", ["decode_b64", "draft_extend_b16"])
+def test_reuse_modes_sampled(va, name):
+    p = W.CONFIGS[name]()
+    pg = p.to(dev())
+    out = run_gpu(va, pg)
+    gen = torch.Generator().manual_seed(5)
+    bsel = torch.randperm(p.bs, generator=gen)[:6].tolist()
+    sel = [(b, h) for b in bsel for h in (0, 7, 15)]
+    ref = oracle.verify_attn(p.q, p.k_ext, p.v_ext, p.k_buf, p.v_buf, p.qo_indptr, p.kv_indptr,
+                             p.kv_indices, p.sm_scale, p.k_scale, p.v_scale, select=sel)
+    rows = np.zeros(out.shape, dtype=bool)
+    for b, h in sel:
+        rows[b * p.l_ext:(b + 1) * p.l_ext, h] = True
+    assert_close(out, ref, BF16_TOL, name + " sampled", mask=rows)
+
+
+def test_decode_small_full(va):
+    p = W.make_problem([3000, 1, 0, 700, 4096], 1, 16, 2, 256, 256, pool_factor=2, permute=True, seed=60,
+                       name="decode small")
+    out = run_gpu(va, p.to(dev()))
+    assert_close(out, oracle.verify_attn(p.q, p.k_ext, p.v_ext, p.k_buf, p.v_buf, p.qo_indptr, p.kv_indptr,
+                                         p.kv_indices, p.sm_scale, p.k_scale, p.v_scale),
+                 BF16_TOL, p.name)
