@@ -116,23 +116,7 @@ typedef struct {
     int64_t combine_blocks;  /* grid of the combine kernel (one 64-thread workgroup per output row) */
     size_t workspace_bytes;  /* bytes of workspace the two passes need */
     size_t partial_bytes;    /* of which: bf16 partial outputs (the fp32 log-sum-exps follow) */
-    int32_t balance;         /* 1: long ranges are balanced at run time (below) */
-    int32_t range_tiles;     /* tile_tokens-tiles of a full range (mode 0) */
-    size_t thief_offset;     /* balance: workspace offset of the stolen parts' partials */
-    size_t ctrl_offset;      /* balance: workspace offset of the per-work-item control words */
 } va_plan_t;
-/* Run-time balancing (balance = 1).  Chosen only by the automatic split
- * (split_tokens = n_splits = 0) when every range spans at least 32 tiles, a
- * KV head's rows fit one 32-row query block and no sequence has more than 64
- * ranges.  The prefix grid is then twice the work-item count: the second half
- * are thief workgroups, dispatched as the first half retire; each takes the
- * back part of the range with the most work left (at most once per range)
- * and the combine pass merges that part's partial like any other range.  Which workgroup
- * computes which tokens then depends on timing, so results vary between calls
- * within floating-point rounding; an explicit split_tokens or n_splits gives
- * a static, bitwise reproducible schedule, and so does a call whose workspace
- * holds the static layout (workspace_bytes of the same descriptor with a
- * split) but not the balancing areas. */
 
 /* Validate a descriptor (host only; no HIP call).
  * Mirrors can_handle() in verify_splitkv.py, which accepts only causal topk=1

@@ -22,15 +22,11 @@ ARCH = "gfx950"
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU forms.
 # kernarg preload: the first 8 kernel arguments of every kernel (the pointers
 # and sizes the range lookup needs) arrive in SGPRs at wave launch.
-# atomic optimizer off: the prefix kernel's claims are single-lane atomics
-# whose answer is read a whole tile later; the optimizer's wave-wide rewrite
-# reads it back at once and so waits for every outstanding load there.
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall",
           "-I", INCLUDE, "-I", CSRC]
 DEVICE = ["-x", "hip", "--offload-arch=" + ARCH,
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          "-mllvm", "-amdgpu-kernarg-preload-count=8",
-          "-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]
+          "-mllvm", "-amdgpu-kernarg-preload-count=8"]
 
 SOURCES = ["va_kernels.hip", "va_aux.hip", "va_plan.cpp", "va_api.cpp", "va_aux_api.cpp"]
 

@@ -49,17 +49,6 @@ int check_align(const void *const *ptrs, int n)
     return VA_OK;
 }
 
-// The plan a call runs with: balancing needs its own areas in the workspace;
-// a workspace with room for the static schedule only (a runner that sized it
-// for another shape) runs the static schedule instead.
-int plan_for_workspace(const va_desc_t *desc, int32_t l_ext, size_t ws_bytes, va_plan_t *plan)
-{
-    int rc = make_plan(desc, l_ext, 0, plan);
-    if (rc == VA_OK && plan->balance && ws_bytes < plan->workspace_bytes)
-        rc = make_plan(desc, l_ext, 0, plan, false);
-    return rc;
-}
-
 int check_workspace(const va_plan_t &plan, const void *ws, size_t ws_bytes)
 {
     if (plan.workspace_bytes == 0)
@@ -95,17 +84,6 @@ int prefix_impl(const void *q, const void *k_buf, const void *v_buf, const int32
     p.kv_indices = kv_indices;
     p.part_o = (uint16_t *)workspace;
     p.part_lse = (float *)((char *)workspace + plan.partial_bytes);
-    p.ctrl = nullptr;
-    p.part_o_thief = nullptr;
-    p.part_lse_thief = nullptr;
-    // work items (= workgroups without balancing; the thieves follow them)
-    p.n_items = (int32_t)(plan.range_slots * desc->h_kv * plan.row_chunks);
-    p.range_tiles = plan.range_tiles;
-    if (plan.balance) {
-        p.ctrl = (uint64_t *)((char *)workspace + plan.ctrl_offset);
-        p.part_o_thief = (uint16_t *)((char *)workspace + plan.thief_offset);
-        p.part_lse_thief = (float *)((char *)workspace + plan.thief_offset + plan.partial_bytes);
-    }
     const int eb = desc->kv_dtype == VA_DTYPE_FP8_E4M3FN ? 1 : 2;
     p.q_s0 = desc->q_stride[0];
     p.q_s1 = desc->q_stride[1];
@@ -125,13 +103,6 @@ int prefix_impl(const void *q, const void *k_buf, const void *v_buf, const int32
     p.split_tokens = plan.split_tokens > 0 ? plan.split_tokens : 1;
     p.n_splits = plan.n_splits > 0 ? plan.n_splits : 1;
     const int qb = query_blocks_for(plan.rows < kRowChunk ? plan.rows : kRowChunk);
-    if (plan.balance) {
-        const int er = launch_reset_ctrl(p.ctrl, p.n_items, stream);
-        if (er != 0) {
-            set_error("control word reset launch: %s", hip_error_string(er));
-            return VA_ERR_DEVICE;
-        }
-    }
     int e = launch_prefix(p, desc->head_dim, desc->kv_dtype == VA_DTYPE_FP8_E4M3FN, qb,
                           plan.prefix_blocks, stream);
     if (e != 0) {
@@ -156,15 +127,6 @@ int combine_impl(const void *q, const void *k_ext, const void *v_ext, const int3
     c.kv_indptr = kv_indptr;
     c.part_o = (const uint16_t *)workspace;
     c.part_lse = (const float *)((const char *)workspace + plan.partial_bytes);
-    c.ctrl = nullptr;
-    c.part_o_thief = nullptr;
-    c.part_lse_thief = nullptr;
-    c.row_chunks = plan.row_chunks;
-    if (plan.balance && plan.prefix_blocks > 0) {
-        c.ctrl = (const uint64_t *)((const char *)workspace + plan.ctrl_offset);
-        c.part_o_thief = (const uint16_t *)((const char *)workspace + plan.thief_offset);
-        c.part_lse_thief = (const float *)((const char *)workspace + plan.thief_offset + plan.partial_bytes);
-    }
     c.out = (uint16_t *)out;
     c.q_s0 = desc->q_stride[0];
     c.q_s1 = desc->q_stride[1];
@@ -248,7 +210,7 @@ VA_API int verify_attn_prefix(const void *q, const void *k_buf, const void *v_bu
     if ((rc = va::check_scales(sm_scale, k_scale, v_scale)) != VA_OK)
         return rc;
     va_plan_t plan;
-    if ((rc = va::plan_for_workspace(desc, l_ext, workspace_bytes, &plan)) != VA_OK)
+    if ((rc = va::make_plan(desc, l_ext, 0, &plan)) != VA_OK)
         return rc;
     if ((rc = va::check_workspace(plan, workspace, workspace_bytes)) != VA_OK)
         return rc;
@@ -273,7 +235,7 @@ VA_API int verify_attn_combine(const void *q, const void *k_ext, const void *v_e
     if ((rc = va::check_scales(sm_scale, 1.0f, 1.0f)) != VA_OK)
         return rc;
     va_plan_t plan;
-    if ((rc = va::plan_for_workspace(desc, l_ext, workspace_bytes, &plan)) != VA_OK)
+    if ((rc = va::make_plan(desc, l_ext, 0, &plan)) != VA_OK)
         return rc;
     if ((rc = va::check_workspace(plan, workspace, workspace_bytes)) != VA_OK)
         return rc;
@@ -300,7 +262,7 @@ VA_API int verify_attn_run(const void *q, const void *k_ext, const void *v_ext, 
     if ((rc = va::check_scales(sm_scale, k_scale, v_scale)) != VA_OK)
         return rc;
     va_plan_t plan;
-    if ((rc = va::plan_for_workspace(desc, l_ext, workspace_bytes, &plan)) != VA_OK)
+    if ((rc = va::make_plan(desc, l_ext, 0, &plan)) != VA_OK)
         return rc;
     if ((rc = va::check_workspace(plan, workspace, workspace_bytes)) != VA_OK)
         return rc;
@@ -332,7 +294,7 @@ VA_API int verify_attn_combine_tree(const void *q, const void *k_ext, const void
     if ((rc = va::check_scales(sm_scale, 1.0f, 1.0f)) != VA_OK)
         return rc;
     va_plan_t plan;
-    if ((rc = va::plan_for_workspace(desc, l_ext, workspace_bytes, &plan)) != VA_OK)
+    if ((rc = va::make_plan(desc, l_ext, 0, &plan)) != VA_OK)
         return rc;
     if ((rc = va::check_workspace(plan, workspace, workspace_bytes)) != VA_OK)
         return rc;
@@ -362,7 +324,7 @@ VA_API int verify_attn_run_tree(const void *q, const void *k_ext, const void *v_
     if ((rc = va::check_scales(sm_scale, k_scale, v_scale)) != VA_OK)
         return rc;
     va_plan_t plan;
-    if ((rc = va::plan_for_workspace(desc, l_ext, workspace_bytes, &plan)) != VA_OK)
+    if ((rc = va::make_plan(desc, l_ext, 0, &plan)) != VA_OK)
         return rc;
     if ((rc = va::check_workspace(plan, workspace, workspace_bytes)) != VA_OK)
         return rc;
@@ -395,7 +357,7 @@ VA_API int verify_attn_prefix_paged(const void *q, const void *k_buf, const void
     if ((rc = va::check_scales(sm_scale, k_scale, v_scale)) != VA_OK)
         return rc;
     va_plan_t plan;
-    if ((rc = va::plan_for_workspace(desc, l_ext, workspace_bytes, &plan)) != VA_OK)
+    if ((rc = va::make_plan(desc, l_ext, 0, &plan)) != VA_OK)
         return rc;
     if ((rc = va::check_workspace(plan, workspace, workspace_bytes)) != VA_OK)
         return rc;
@@ -425,7 +387,7 @@ VA_API int verify_attn_run_paged(const void *q, const void *k_ext, const void *v
     if ((rc = va::check_scales(sm_scale, k_scale, v_scale)) != VA_OK)
         return rc;
     va_plan_t plan;
-    if ((rc = va::plan_for_workspace(desc, l_ext, workspace_bytes, &plan)) != VA_OK)
+    if ((rc = va::make_plan(desc, l_ext, 0, &plan)) != VA_OK)
         return rc;
     if ((rc = va::check_workspace(plan, workspace, workspace_bytes)) != VA_OK)
         return rc;

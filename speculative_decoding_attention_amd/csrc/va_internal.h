@@ -29,17 +29,6 @@ constexpr int prefix_resident_per_cu(int qblocks) { return qblocks == 1 ? 2 : 1;
 // Draft tokens a tree mask may cover (the combine kernel keeps a row's
 // visibility in one 64-bit ballot).
 constexpr int kMaxTreeDrafts = 64;
-// Dynamic balancing of long ranges (one-query-block shape only).  Each work
-// item has a 64-bit control word in the workspace: low half = tiles claimed
-// by the owner (0 until the owner has started), high half = end of the
-// owner's part (kStealNone until a thief takes the back of the range).
-constexpr int kStealChunk = 4;               // tiles per owner claim
-constexpr int kStealMin = 6;                 // unclaimed tiles worth a steal
-constexpr uint32_t kStealNone = 0xffffffffu;
-constexpr uint32_t kStealDone = 1u << 24;     // added to the claimed count: nothing to take here
-constexpr int kStealMinTilesPerRange = 32;   // planner: ranges at least this long
-constexpr int kStealMaxRangesPerSeq = 64;    // the combine keeps stolen flags in one ballot
-constexpr int kStealRounds = 4;              // searches of a thief workgroup (lost races retry)
 // Smallest range the heuristic chooses; ranges are multiples of this.
 constexpr int kSplitQuantum = 64;
 
@@ -67,13 +56,6 @@ struct PrefixParams {
     int32_t page_size;
     uint16_t *part_o;  // [range_slots * h_kv, rows, D] bf16 (round to nearest even)
     float *part_lse;   // [range_slots * h_kv, rows]    fp32 (natural log)
-    // dynamic balancing (NULL ctrl: off): control words per work item and the
-    // partials of stolen back parts (same layout as part_o / part_lse)
-    uint64_t *ctrl;
-    uint16_t *part_o_thief;
-    float *part_lse_thief;
-    int32_t n_items;            // work items (= prefix workgroups)
-    int32_t range_tiles;        // tiles of a full range (victim estimate)
     int64_t q_s0, q_s1;        // elements
     uint32_t kb_s0, vb_s0;     // pool row strides, bytes (< 2^32, checked on the host)
     int64_t kb_s1, vb_s1;      // pool head strides, bytes
@@ -92,10 +74,6 @@ struct CombineParams {
     const uint16_t *part_o;
     const float *part_lse;
     uint16_t *out;
-    const uint64_t *ctrl;         // dynamic balancing control words, or NULL
-    const uint16_t *part_o_thief;
-    const float *part_lse_thief;
-    int32_t row_chunks;
     const uint8_t *mask;          // tree mask bytes, or NULL for the causal draft block
     const int64_t *mask_indptr;   // [bs + 1] byte offsets of each sequence's mask
     int64_t q_s0, q_s1, ke_s0, ke_s1, ve_s0, ve_s1, o_s0, o_s1;  // elements
@@ -139,13 +117,11 @@ int launch_build_kv_indices(const BuildIndicesParams &p, void *stream);
 int launch_prefix(const PrefixParams &p, int head_dim, bool kv_fp8, int qblocks,
                   int64_t blocks, void *stream);
 int launch_combine(const CombineParams &p, int head_dim, int64_t blocks, void *stream);
-int launch_reset_ctrl(uint64_t *ctrl, int64_t n, void *stream);
 const char *hip_error_string(int err);
 
 // Host-side validation and planning (defined in va_plan.cpp).
 int check_desc(const va_desc_t *d, int32_t l_ext);
-int make_plan(const va_desc_t *d, int32_t l_ext, int32_t num_cus, va_plan_t *plan,
-              bool allow_balance = true);
+int make_plan(const va_desc_t *d, int32_t l_ext, int32_t num_cus, va_plan_t *plan);
 int current_device_cus(int32_t *cus);
 void set_error(const char *fmt, ...);
 void clear_error();

@@ -203,16 +203,7 @@ __device__ __forceinline__ void dma4(const void *g, uint32_t lds_base)
                  :: "s"(lds_base), "v"(g) : "memory", "m0");
 }
 
-// The same copy with device-scope coherence (sc1): the dword is read where
-// device-scope atomics are performed, not from a stale cached line.
-__device__ __forceinline__ void dma4_coherent(const void *g, uint32_t lds_base)
-{
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off sc1"
-                 :: "s"(lds_base), "v"(g) : "memory", "m0");
-}
-
-// Wait until at most N vector-memory operations of this wave are outstanding
-// (loads, and stores and atomics until the memory system has performed them).
+// Wait until at most N vector-memory loads of this wave are outstanding.
 template <int N>
 __device__ __forceinline__ void wait_vm()
 {
@@ -350,7 +341,6 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64) void prefix_kernel(
 
     __shared__ __attribute__((aligned(1024))) uint8_t s_ring[NBUF * G::STAGE];
     __shared__ __attribute__((aligned(16))) int64_t s_idx[NW][G::NIDX][RW];
-    __shared__ __attribute__((aligned(8))) uint32_t s_ctl[4];  // balancing: [0..1] control word, [2..3] taken item / tile
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -358,125 +348,26 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64) void prefix_kernel(
     const int l32 = lane & 31;   // token (A) / query row (B, C) within a 32 block
     const int half = lane >> 5;  // k half of the operands
 
-    // ---- kernel arguments ----
+    // ---- work item: (range, KV head, row chunk) ----
     // index pointers of the first 64 sequences, then the remaining kernel
     // arguments while those loads are in flight
     const SeqChunk first = load_seq_chunk(kv_indptr, qo_indptr, bs, 0);
     asm volatile("" ::"s"(p.q), "s"(p.kv_indices), "s"(p.k_buf), "s"(p.v_buf), "s"(p.kb_s1), "s"(p.vb_s1),
                  "s"(p.kb_s0), "s"(p.vb_s0), "s"(p.q_s0), "s"(p.q_s1), "s"(p.group), "s"(p.l_ext), "s"(p.rows)
                  : "memory");
-    const uint32_t ring = lds_offset(s_ring);
-    // run-time balancing of long ranges (2-stage ring only): p.ctrl holds one
-    // control word per work item, (owner end << 32) | tiles claimed by the owner
-    const bool dyn = NBUF == 2 && p.ctrl != nullptr;
-    static_assert(kStealChunk >= 3, "a claim is answered before the claimed chunk is issued");
-
-    // ---- work item: (range, KV head, row chunk) ----
-    // Workgroups past p.n_items exist only with balancing on: each takes the
-    // back part of another item's range (tiles win.. of it) and writes that
-    // part's partial to the thieves' area.  They are dispatched as the owners'
-    // workgroups retire, so they start where work has run out.
-    uint32_t item = blockIdx.x;
-    int win = 0;
-    if (dyn && item >= (uint32_t)p.n_items) {
-        // Wave 0 reads 64 control words spread over the items, picks the item
-        // with the most unclaimed tiles (estimated from a full range's tile
-        // count) and, with the exact tile count of that range, takes the back
-        // part of what is unclaimed with one compare-and-swap that sets the
-        // owner's end.  The split point leaves the owner, which is up to two
-        // chunks behind its claims, about as much as the thief.  A range is
-        // taken from at most once; a lost race or a short range costs a retry,
-        // a sample with nothing to take ends the workgroup.
-        uint32_t pick = item * 0x9E3779B1u;
-        int victim = -1, from = 0;  // victim -1: nothing to take; -2: retry
-        for (int round = 0; round < kStealRounds; ++round) {
-            if (wave == 0) {
-                int vic = -1, fr = 0;
-                const uint32_t n_items = (uint32_t)p.n_items;
-                // odd stride: the samples cover every KV head (items of one
-                // range differ in the head index, the fastest varying part)
-                const uint32_t stride = (n_items > 64 ? n_items / 64 : 1) | 1u;
-                const uint32_t it = (pick + (uint32_t)lane * stride) % n_items;
-                const uint64_t w = __hip_atomic_load(p.ctrl + it, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                // owners not started yet (claimed count 0) are left alone
-                const int est = (uint32_t)(w >> 32) == kStealNone && (uint32_t)w != 0 ? p.range_tiles - (int)(uint32_t)w
-                                                                                     : -1;
-                int best = est;
-#pragma unroll
-                for (int off = 32; off > 0; off >>= 1)
-                    best = max(best, __shfl_xor(best, off));
-                if (best >= kStealMin) {
-                    vic = -2;
-                    const int who = __ffsll((unsigned long long)__ballot(est == best)) - 1;
-                    const uint32_t v = (uint32_t)__shfl((int)it, who);
-                    uint64_t cur = ((uint64_t)(uint32_t)__shfl((int)(uint32_t)(w >> 32), who) << 32) |
-                                   (uint32_t)__shfl((int)(uint32_t)w, who);
-                    const Range vr = locate_range(kv_indptr, qo_indptr, bs, mode, split_tokens, n_splits,
-                                                  (v / (uint32_t)row_chunks) / (uint32_t)h_kv, first);
-                    const int cap = vr.valid ? (vr.end - vr.start + TN - 1) / TN : 0;
-                    for (int a = 0; a < 4; ++a) {
-                        const int h = (int)(uint32_t)cur;
-                        if ((uint32_t)(cur >> 32) != kStealNone || cap - h < kStealMin)
-                            break;
-                        const int f = max(h, (h + cap - kStealChunk + 1) / 2);
-                        uint64_t seen = cur;
-                        int ok = 0;
-                        if (lane == 0)
-                            ok = __hip_atomic_compare_exchange_strong(
-                                p.ctrl + v, &seen, ((uint64_t)(uint32_t)f << 32) | (uint32_t)h, __ATOMIC_RELAXED,
-                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        ok = __builtin_amdgcn_readfirstlane(ok);
-                        cur = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(seen >> 32))
-                               << 32) |
-                              (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)seen);
-                        if (ok) {
-                            vic = (int)v;
-                            fr = f;
-                            break;
-                        }
-                    }
-                }
-                if (lane == 0) {
-                    s_ctl[2] = (uint32_t)vic;
-                    s_ctl[3] = (uint32_t)fr;
-                }
-            }
-            lds_barrier();
-            victim = (int)__builtin_amdgcn_readfirstlane(s_ctl[2]);
-            from = (int)__builtin_amdgcn_readfirstlane(s_ctl[3]);
-            if (victim != -2)
-                break;
-            lds_barrier();  // every wave has read s_ctl before wave 0 writes it again
-            pick = pick * 1664525u + 1013904223u;  // next sample set
-        }
-        if (victim < 0)
-            return;
-        item = (uint32_t)victim;
-        win = from;
-    }
-    const bool thief = win > 0;
-    // An owner item with nothing a thief could take (surplus slot, empty or
-    // single-chunk range) says so at once: its claimed count jumps past any
-    // range, so samplers skip it instead of spending a search on it.
-    auto mark_done = [&]() {
-        if (dyn && !thief && tid == 0)
-            (void)__hip_atomic_fetch_add(p.ctrl + item, (uint64_t)kStealDone, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
-    };
-    const int rc = (int)(item % (uint32_t)row_chunks);
-    const uint32_t t1 = item / (uint32_t)row_chunks;
+    const uint32_t blk = blockIdx.x;
+    const int rc = (int)(blk % (uint32_t)row_chunks);
+    const uint32_t t1 = blk / (uint32_t)row_chunks;
     const int kvh = (int)(t1 % (uint32_t)h_kv);
     const int64_t cidx = t1 / (uint32_t)h_kv;
-    Range rg = locate_range(kv_indptr, qo_indptr, bs, mode, split_tokens, n_splits, cidx, first);
-    if (!rg.valid) {
-        mark_done();
+    const Range rg = locate_range(kv_indptr, qo_indptr, bs, mode, split_tokens, n_splits, cidx, first);
+    if (!rg.valid)
         return;  // surplus slot of the static grid: never read by the combine pass
-    }
     const int64_t slot = cidx * h_kv + kvh;
     const int rows = p.rows;
     const int row0 = rc * kRowChunk;
-    uint16_t *po = (thief ? p.part_o_thief : p.part_o) + slot * (int64_t)rows * D;
-    float *pl = (thief ? p.part_lse_thief : p.part_lse) + slot * (int64_t)rows;
+    uint16_t *po = p.part_o + slot * (int64_t)rows * D;
+    float *pl = p.part_lse + slot * (int64_t)rows;
 
     if (rg.start >= rg.end) {
         // Empty range: output 0 and log-sum-exp -inf, so the merge weight is
@@ -486,15 +377,14 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64) void prefix_kernel(
             po[(int64_t)(row0 + e / D) * D + (e % D)] = 0;
         if (tid < nr)
             pl[row0 + tid] = -INFINITY;
-        mark_done();
         return;
     }
-    rg.start += win * TN;  // a taken back part is never empty
 
     const int64_t kv0 = (int64_t)rg.kv_base + rg.start;
     const int len = rg.end - rg.start;
     const int nt = (len + TN - 1) / TN;
     const int qo = rg.qo;
+    const uint32_t ring = lds_offset(s_ring);
 
     // ---- query tile -> ring stage NBUF-1 (bf16 rows of D, row-major) ----
     {
@@ -644,25 +534,7 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64) void prefix_kernel(
         oacc[db] = f32x16_t{};
 
     const float qk_scale = p.qk_scale_log2;
-    // Balanced range, owner side: the owner holds tiles [0, own_nt).  At the
-    // first tile t of chunk c >= 1 it claims chunk c + 1: an atomic add without
-    // return, performed by the next loop-top wait; at tile t + 1 wave 0 copies
-    // the control word into s_ctl (device-coherent read), and at tile t + 2
-    // every wave reads it after the barrier.  The claim holds up to the owner
-    // end a thief may have set; that end is final (the thief saw the claims
-    // made before its compare-and-swap, so the end is never below own_nt).
-    // At its start the owner holds its first two chunks (one add) or, with
-    // no more than that, says there is nothing to take.
-    const bool claims = dyn && !thief && nt > 2 * kStealChunk;
-    if (!claims)
-        mark_done();
-    else if (tid == 0)
-        (void)__hip_atomic_fetch_add(p.ctrl + item, (uint64_t)(2 * kStealChunk), __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT);
-    int own_nt = claims ? 2 * kStealChunk : nt;
-    bool claiming = claims;
-    int phase = 0;  // 1: claim made at tile t - 1; 2: control word copied at tile t - 1
-    for (int t = 0; t < own_nt; ++t) {
+    for (int t = 0; t < nt; ++t) {
         // tile t's copies by this wave are complete; then everyone's are
         if constexpr (NBUF == 4) {
             const int after = nt - 1 - t;
@@ -676,29 +548,12 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64) void prefix_kernel(
             wait_vm<0>();  // tile t was the last copy issued
         }
         lds_barrier();
-        if (phase == 2) {  // the control word after the claim made at tile t - 2
-            const uint32_t tail = __builtin_amdgcn_readfirstlane(s_ctl[1]);
-            // (tile t = c * kStealChunk + 2; the claim covered chunk c + 1)
-            own_nt = tail != kStealNone ? (int)tail : min((t / kStealChunk + 2) * kStealChunk, nt);
-            claiming = tail == kStealNone && own_nt < nt;
-            phase = 0;
-        } else if (phase == 1) {
-            if (wave == 0 && lane < 2)
-                dma4_coherent((const uint32_t *)(p.ctrl + item) + lane, lds_offset(s_ctl));
-            phase = 2;
-        }
-        if (claiming && t % kStealChunk == 0 && t > 0) {
-            if (tid == 0)
-                (void)__hip_atomic_fetch_add(p.ctrl + item, (uint64_t)kStealChunk, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT);
-            phase = 1;
-        }
 
         // step j = t + NBUF - 1 into the stage tile t-1 used (everyone is past it)
         {
             const int j = t + NBUF - 1;
             issue_idx(j + 2);
-            if (j < own_nt) {
+            if (j < nt) {
                 wait_vm<4 * NIKW + 2>();  // index slot j, copied two steps ago
                 issue_tile(j);
             }
@@ -1022,20 +877,6 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     } else {
         vis = di >= 63 ? ~0ull : ((2ull << di) - 1);
     }
-    // balanced ranges (at most 64 per sequence): a range whose control word
-    // holds an owner end had its back part taken; that part's log-sum-exp is
-    // merged like a range's, anything else in the thieves' area is never used
-    uint64_t stolen = 0;
-    float lse_t = -INFINITY;
-    if (p.ctrl && count > 0) {
-        const int64_t sl = base + (lane < count ? lane : last);
-        const uint64_t w = __hip_atomic_load(p.ctrl + (sl * p.h_kv + kvh) * p.row_chunks + r / kRowChunk,
-                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const float x = p.part_lse_thief[(sl * p.h_kv + kvh) * p.rows + r];
-        const bool st = lane < count && (uint32_t)(w >> 32) != kStealNone;
-        stolen = __ballot(st);
-        lse_t = st ? x : -INFINITY;
-    }
     float kd[PRE_D][VPL], vd[PRE_D][VPL];
 #pragma unroll
     for (int j = 0; j < PRE_D; ++j) {
@@ -1045,7 +886,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     }
 
     // ---- (a) prefix ranges ----
-    float m = fmaxf(lse0, lse_t);
+    float m = lse0;
     for (int s = 64 + lane; s < count; s += 64)
         m = fmaxf(m, lse_row[s * lse_step]);
     m = wave_max(m);
@@ -1055,7 +896,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     for (int v = 0; v < VPL; ++v)
         acc[v] = 0.0f;
     if (m > -INFINITY) {  // an empty range (lse -inf) has weight 0 and output 0
-        float e = (lane < count ? __expf(lse0 - m) : 0.0f) + __expf(lse_t - m);  // lse_t -inf: 0
+        float e = lane < count ? __expf(lse0 - m) : 0.0f;
         for (int s = 64 + lane; s < count; s += 64)
             e += __expf(lse_row[s * lse_step] - m);
         den = wave_sum(e);
@@ -1079,28 +920,6 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
 #pragma unroll
                 for (int v = 0; v < VPL; ++v)
                     acc[v] += w * ov[i][v];
-            }
-        }
-        // taken back parts, in load batches of 8 (slots past the last one
-        // re-read a taken part and get weight 0)
-        const uint16_t *t_row = p.part_o_thief + (((int64_t)base * p.h_kv + kvh) * p.rows + r) * D + d0;
-        for (uint64_t left = stolen; left != 0;) {
-            int si[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                si[i] = left != 0 ? (int)__builtin_ctzll(left) : -1;
-                left &= left - 1;
-            }
-            float tv[8][VPL];
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                load_bf16_row<VPL>(t_row + (si[i] >= 0 ? si[i] : si[0]) * o_step, tv[i]);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float w = si[i] >= 0 ? __expf(__shfl(lse_t, si[i] >= 0 ? si[i] : 0) - m) : 0.0f;
-#pragma unroll
-                for (int v = 0; v < VPL; ++v)
-                    acc[v] += w * tv[i][v];
             }
         }
     }
@@ -1179,15 +998,6 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
         orow[v] = (uint16_t)f32_to_bf16_rne((wp * acc[v] + wd * od[v]) * inv);
 }
 
-// ---------------------------------------------------- balancing control reset ---
-// Every control word starts as (no owner end, owner not started).
-__global__ __launch_bounds__(256) void reset_ctrl_kernel(uint64_t *ctrl, int64_t n)
-{
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i < n)
-        __hip_atomic_store(ctrl + i, (uint64_t)kStealNone << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // ----------------------------------------------------------------- launch ---
 template <bool FP8, int D>
 static int launch_prefix_qb(const PrefixParams &p, int qblocks, int64_t blocks, hipStream_t s)
@@ -1231,13 +1041,6 @@ int launch_combine(const CombineParams &p, int head_dim, int64_t blocks, void *s
     default: hipLaunchKernelGGL((combine_kernel<256>), grid, block, 0, s, VA_COMBINE_ARGS); break;
 #undef VA_COMBINE_ARGS
     }
-    return (int)hipGetLastError();
-}
-
-int launch_reset_ctrl(uint64_t *ctrl, int64_t n, void *stream)
-{
-    dim3 grid((unsigned)((n + 255) / 256)), block(256);
-    hipLaunchKernelGGL(reset_ctrl_kernel, grid, block, 0, (hipStream_t)stream, ctrl, n);
     return (int)hipGetLastError();
 }
 

@@ -129,7 +129,7 @@ int current_device_cus(int32_t *cus)
     return VA_OK;
 }
 
-int make_plan(const va_desc_t *d, int32_t l_ext, int32_t num_cus, va_plan_t *plan, bool allow_balance)
+int make_plan(const va_desc_t *d, int32_t l_ext, int32_t num_cus, va_plan_t *plan)
 {
     if (!plan)
         return fail(VA_ERR_NULL_ARG, "plan is NULL");
@@ -183,25 +183,6 @@ int make_plan(const va_desc_t *d, int32_t l_ext, int32_t num_cus, va_plan_t *pla
     const int64_t l_bytes = align_up(slots * rows * 4, 256);
     p.partial_bytes = (size_t)o_bytes;
     p.workspace_bytes = (size_t)(o_bytes + l_bytes);
-    if (p.mode == 0)
-        p.range_tiles = (int32_t)((p.split_tokens + p.tile_tokens - 1) / p.tile_tokens);
-    // Run-time balancing: automatic split, one 32-row query block, ranges of
-    // at least kStealMinTilesPerRange tiles and at most kStealMaxRangesPerSeq
-    // ranges per sequence (T / c bounds ceil(n_b / c) for every sequence).
-    const bool auto_split = d->split_tokens == 0 && d->n_splits == 0;
-    if (allow_balance && auto_split && p.prefix_blocks > 0 && rows <= 32 && p.range_tiles >= kStealMinTilesPerRange &&
-        (T + p.split_tokens - 1) / p.split_tokens <= kStealMaxRangesPerSeq) {
-        // one control word per work item; as many thief workgroups as items
-        // follow the items in the grid (a range is taken from at most once)
-        const int64_t n_items = p.prefix_blocks;
-        if (2 * n_items <= INT32_MAX) {
-            p.balance = 1;
-            p.prefix_blocks = 2 * n_items;
-            p.thief_offset = (size_t)(o_bytes + l_bytes);
-            p.ctrl_offset = p.thief_offset + (size_t)(o_bytes + l_bytes);
-            p.workspace_bytes = p.ctrl_offset + (size_t)align_up(n_items * 8, 256);
-        }
-    }
     *plan = p;
     clear_error();
     return VA_OK;
@@ -256,6 +237,6 @@ VA_API const char *verify_attn_strerror(int code)
 
 VA_API const char *verify_attn_last_error(void) { return va::last_error(); }
 
-VA_API int verify_attn_version(void) { return 201; }
+VA_API int verify_attn_version(void) { return 200; }
 
 }  // extern "C"

@@ -125,53 +125,6 @@ def test_range_slots_bound_every_ragged_batch(seed):
         assert sum(math.ceil(n / c) for n in lens) <= plan.range_slots
 
 
-def _long_meta(bs=4, n=65536, l_ext=8, h_q=32, h_kv=8):
-    return meta_problem(bs=bs, n=n, l_ext=l_ext, h_q=h_q, h_kv=h_kv)
-
-
-def test_balancing_is_planned_for_long_ranges():
-    # 4 x 64k prefix, 32/8 heads, D=256 on 256 CUs: 4096-token ranges of 128
-    # tiles, 16 ranges per sequence -> balanced; the grid doubles (thieves
-    # follow the items) and the workspace gains the thieves' partials and
-    # one 8-byte control word per item
-    plan = va.verify_attn_plan(va.make_desc(**_long_meta()), 8, 256)
-    assert plan.balance == 1 and plan.split_tokens == 4096 and plan.range_tiles == 128
-    n_items = plan.range_slots * 8 * plan.row_chunks
-    assert plan.prefix_blocks == 2 * n_items
-    o_bytes = plan.partial_bytes
-    assert plan.thief_offset >= o_bytes + plan.range_slots * 8 * 32 * 4
-    assert plan.ctrl_offset >= plan.thief_offset + o_bytes
-    assert plan.workspace_bytes >= plan.ctrl_offset + 8 * n_items
-    assert plan.thief_offset % 256 == 0 and plan.ctrl_offset % 256 == 0
-
-
-@pytest.mark.parametrize("kw,l_ext,why", [
-    (dict(split_tokens=4096), 8, "explicit split: static schedule"),
-    (dict(n_splits=16), 8, "the pages' split rule: static schedule"),
-    (dict(), 16, "64 rows per KV head: two query blocks"),
-])
-def test_balancing_off(kw, l_ext, why):
-    meta = _long_meta(l_ext=l_ext, **{})
-    meta.update(kw)
-    meta["q"] = torch.empty(4 * l_ext, 32, 256, dtype=torch.bfloat16, device="meta")
-    meta["out"] = meta["q"]
-    meta["k_ext"] = torch.empty(4 * l_ext, 8, 256, dtype=torch.bfloat16, device="meta")
-    meta["v_ext"] = meta["k_ext"]
-    plan = va.verify_attn_plan(va.make_desc(**meta), l_ext, 256)
-    assert plan.balance == 0, why
-    assert plan.prefix_blocks == plan.range_slots * 8 * plan.row_chunks
-
-
-def test_balancing_off_for_short_ranges():
-    # the headline 8 x 8k shape: 256-token ranges (8 tiles) stay static
-    plan = va.verify_attn_plan(va.make_desc(**meta_problem(bs=8, n=8192)), 4, 256)
-    assert plan.balance == 0
-    # one long sequence with one KV head: 512 ranges of it exceed the
-    # combine's 64-range limit for balanced sequences
-    plan = va.verify_attn_plan(va.make_desc(**_long_meta(bs=1, n=1 << 20, h_q=8, h_kv=1, l_ext=4)), 4, 256)
-    assert plan.balance == 0
-
-
 def test_pages_split_rule_mode():
     plan = va.verify_attn_plan(desc_of(n_splits=8), 4, 256)
     assert plan.mode == 1 and plan.n_splits == 8 and plan.range_slots == 3 * 8
