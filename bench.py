@@ -337,27 +337,59 @@ def time_extensions(torch, va, W, steps, replicas):
     return res
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(torch, W, p_dev, min_seconds=10.0, max_passes=8):
-    """The fp64 oracle on the host cores over the whole headline batch."""
+    """The fp64 oracle on the host cores over the whole headline batch, and on
+    one thread over a bounded sample of it (sequence 0, every head)."""
     import oracle
     p = p_dev.to("cpu")
     args = (p.q, p.k_ext, p.v_ext, p.k_buf, p.v_buf, p.qo_indptr, p.kv_indptr, p.kv_indices,
             p.sm_scale, p.k_scale, p.v_scale)
-    times = []
-    t_start = time.perf_counter()
-    while len(times) < max_passes and (time.perf_counter() - t_start) < min_seconds:
-        t0 = time.perf_counter()
-        oracle.verify_attn(*args)
-        times.append(time.perf_counter() - t0)
-    t = statistics.median(times)
+
+    def median_time(select, budget):
+        times = []
+        t_start = time.perf_counter()
+        while len(times) < max_passes and (time.perf_counter() - t_start) < budget:
+            t0 = time.perf_counter()
+            oracle.verify_attn(*args, select=select)
+            times.append(time.perf_counter() - t0)
+        return statistics.median(times), len(times)
+
+    t, passes = median_time(None, min_seconds)
+    cores = oracle.max_threads()
+    # one thread, sequence 0 with all its heads: 1/bs of the batch
+    sample = [(0, h) for h in range(p.h_q)]
+    oracle.set_threads(1)
+    try:
+        t1, passes1 = median_time(sample, min_seconds / 2)
+    finally:
+        oracle.set_threads(cores)
+    sample_bytes = p.kv_bytes() * p.prefix_lens[0] / max(1, sum(p.prefix_lens))
     return {
         "value": round(p.kv_bytes() / t / 1e9, 4),
         "unit": "GB/s",
-        "cores": oracle.max_threads(),
+        "cores": cores,
         "kind": "oracle",
         "sample": "whole headline batch (all %d sequences x %d heads), median of %d passes; %.3f s/pass"
-                  % (p.bs, p.h_q, len(times), t),
+                  % (p.bs, p.h_q, passes, t),
         "us_per_call": round(t * 1e6, 1),
+        "cpu_model": cpu_model(),
+        "single_thread": {
+            "value": round(sample_bytes / t1 / 1e9, 4),
+            "unit": "GB/s",
+            "sample": "sequence 0 x %d heads (1/%d of the batch) on one thread, median of %d passes; "
+                      "%.3f s/pass" % (p.h_q, p.bs, passes1, t1),
+        },
     }
 
 

@@ -64,6 +64,8 @@ def _bind(path):
     lib.oracle_f64_to_e4m3fn.restype = ctypes.c_uint8
     lib.oracle_f64_to_e4m3fn.argtypes = [ctypes.c_double]
     lib.oracle_max_threads.restype = ctypes.c_int
+    lib.oracle_set_threads.restype = ctypes.c_int
+    lib.oracle_set_threads.argtypes = [ctypes.c_int]
     P = ctypes.c_void_p
     I = ctypes.c_int
     L = ctypes.c_int64
@@ -126,6 +128,12 @@ def f64_to_e4m3fn(x: float) -> int:
 
 def max_threads() -> int:
     return int(_load().oracle_max_threads())
+
+
+def set_threads(n: int) -> int:
+    """OpenMP threads for later calls (n <= 0: all processors); returns the
+    count in effect.  Changes only how long the oracle takes."""
+    return int(_load().oracle_set_threads(int(n)))
 
 
 def _bits16(a) -> np.ndarray:

@@ -365,3 +365,16 @@ int oracle_max_threads(void)
     return 1;
 #endif
 }
+
+/* Threads for the following calls (n <= 0: all processors); returns the count
+ * now in effect.  Only the timing of the oracle changes. */
+int oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    omp_set_num_threads(n > 0 ? n : omp_get_num_procs());
+    return omp_get_max_threads();
+#else
+    (void)n;
+    return 1;
+#endif
+}
