@@ -130,9 +130,23 @@ def test_gqa_ratios(va, hq, hkv):
     check_full(va, W.make_problem([1024, 2048], 4, hq, hkv, 256, seed=53, name="gqa %d/%d" % (hq, hkv)))
 
 
-@pytest.mark.parametrize("l_ext", [1, 2, 4, 8])
+@pytest.mark.parametrize("l_ext", [1, 2, 4, 8, 12, 16])
 def test_extend_lengths(va, l_ext):
+    # l_ext > 8: draft rows past the combine pass's first load batch, and
+    # (16 / 2 heads) 96 or 128 rows per KV head, i.e. two row chunks
     check_full(va, W.make_problem([1024, 1024], l_ext, 16, 2, 256, seed=54, name="l_ext %d" % l_ext))
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(n_splits=4), dict(split_tokens=128)])
+def test_many_sequences(va, kw):
+    # more than 64 sequences: range lookups walk the index pointers in
+    # chunks of 64 (prefix and combine passes); ragged, some prefixes empty
+    g = torch.Generator().manual_seed(71)
+    lens = torch.randint(0, 300, (150,), generator=g)
+    lens[::17] = 0
+    p = W.make_problem(lens.tolist(), 3, 8, 2, 128, pool_factor=2, permute=True, seed=72,
+                       name="150 sequences %s" % kw)
+    check_full(va, p, **kw)
 
 
 def test_kv_scales(va):
