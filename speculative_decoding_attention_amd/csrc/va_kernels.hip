@@ -296,12 +296,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
+// Both shapes keep two waves on every SIMD (two 4-wave workgroups, or one
+// 8-wave workgroup, per CU), so the launch bound holds the kernel to 256
+// registers per lane.
 // The leading scalar arguments are what the first memory round trip needs
 // (the range lookup); they are preloaded into SGPRs at wave launch, so the
 // kv_indptr loads issue without waiting for the kernel-argument fetch.  The
 // same fields are also in p.
 template <bool FP8, int D, int NQB>
-__global__ __launch_bounds__(prefix_waves(NQB) * 64) void prefix_kernel(
+__global__ __launch_bounds__(prefix_waves(NQB) * 64, 2) void prefix_kernel(
     const int32_t *kv_indptr, const int32_t *qo_indptr, int32_t bs, int32_t mode, int32_t split_tokens,
     int32_t n_splits, int32_t h_kv, int32_t row_chunks, const PrefixParams p)
 {
@@ -387,10 +390,14 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64) void prefix_kernel(
     const uint32_t ring = lds_offset(s_ring);
 
     // ---- query tile -> ring stage NBUF-1 (bf16 rows of D, row-major) ----
-    {
-        constexpr int QCH = D / 8;                    // 16-byte chunks per query row
-        constexpr int QI = NQB * 32 * QCH / 64;       // wave-wide copies for the tile
-        for (int i = wave; i < QI; i += NW) {
+    constexpr int QCH = D / 8;                    // 16-byte chunks per query row
+    constexpr int QI = NQB * 32 * QCH / 64;       // wave-wide copies for the tile
+    constexpr int QPW = QI / NW;                  // of which each wave issues
+    static_assert(QI % NW == 0, "query copies split evenly over the waves");
+    auto issue_query = [&]() {
+#pragma unroll
+        for (int k = 0; k < QPW; ++k) {
+            const int i = wave + k * NW;
             const int e = i * 64 + lane;
             const int r = row0 + e / QCH;             // query row of this chunk
             const int rr = r < rows ? r : row0;       // padding rows copy a valid row
@@ -399,7 +406,7 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64) void prefix_kernel(
                                   (int64_t)(kvh * p.group + hg) * p.q_s1 + (e % QCH) * 8;
             dma16(src, __builtin_amdgcn_readfirstlane(ring + (NBUF - 1) * G::STAGE + i * 1024));
         }
-    }
+    };
 
     // ---- copy issue: index slots and K/V tiles ----
     const uint32_t idx_base = lds_offset(&s_idx[wave][0][0]);
@@ -444,35 +451,36 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64) void prefix_kernel(
 
     // prologue: steps j = 0 .. NBUF-2, step j = [index copy of tile j+2][tile j].
     // Loads retire in order, so "index slot j has landed" is "at most the
-    // loads issued after it are outstanding": 2 index copies for j = 0, then
-    // one tile more per step up to the steady-state count.
+    // loads issued after it are outstanding".  Index slot 0 goes out ahead of
+    // the query tile, so tile 0 waits only for its indices; the query tile is
+    // awaited just before the first tile.
     static_assert(NBUF == 2 || NBUF == 4, "wait counts are written for 2- or 4-stage rings");
     issue_idx(0);
+    issue_query();
     issue_idx(1);
     issue_idx(2);
-    wait_vm<2>();
+    wait_vm<QPW + 2>();  // index slot 0: the query copies and 2 index copies came after it
     issue_tile(0);
     if constexpr (NBUF == 4) {
         issue_idx(3);
         if (1 < nt) {
-            wait_vm<2 * NIKW + 2>();
+            wait_vm<2 * NIKW + 2>();  // index slot 1: then slot 2, tile 0, slot 3
             issue_tile(1);
         }
         issue_idx(4);
         if (2 < nt) {
-            wait_vm<4 * NIKW + 2>();
+            wait_vm<4 * NIKW + 2>();  // index slot 2: then tile 0, slot 3, tile 1, slot 4
             issue_tile(2);
         }
-        // the query tile was copied before all of that: 5 index copies and
-        // min(nt, 3) tiles came after it
+        // after the query tile: index slots 1..4 and min(nt, 3) tiles
         if (nt >= 3)
-            wait_vm<5 + 6 * NIKW>();
+            wait_vm<4 + 6 * NIKW>();
         else if (nt == 2)
-            wait_vm<5 + 4 * NIKW>();
+            wait_vm<4 + 4 * NIKW>();
         else
-            wait_vm<5 + 2 * NIKW>();
+            wait_vm<4 + 2 * NIKW>();
     } else {
-        wait_vm<3 + 2 * NIKW>();  // after the query tile: 3 index copies and tile 0
+        wait_vm<2 + 2 * NIKW>();  // after the query tile: index slots 1, 2 and tile 0
     }
     lds_barrier();
 
