@@ -704,69 +704,85 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64, 2) void prefix_kernel(
     wait_vm<0>();  // trailing index copies
     float lrow = l_part + swap_halves(l_part);
 
-    // ---- merge the token shares: waves ts > 0 hand (max, sum, O) to ts = 0 ----
-    // Slots live in the ring, free once every wave is past the last tile.  A
-    // share that saw no token has max -inf and weight exactly 0; share 0 always
-    // saw the range's first token, so the merged max is finite.
+    // ---- merge the token shares ----
+    // Slots live in the ring, free once every wave is past the last tile.  The
+    // 32-column block db of a column share belongs to the wave whose token
+    // share is db mod TS: every wave publishes its (max, sum) and the blocks
+    // it does not own, then merges and stores the blocks it owns, so the LDS
+    // reads and the stores spread over all waves.  A share that saw no token
+    // has max -inf and weight exactly 0; share 0 always saw the range's first
+    // token, so the merged max is finite.
     if constexpr (TS > 1) {
-        // slot: max[32], sum[32], O[32 rows][DWV + 4] (rows padded by 4 floats
-        // so that the 16-byte accesses of 64 lanes spread over all banks)
-        constexpr int OST = DWV + 4;
-        constexpr int SLOT = 64 + 32 * OST;
-        static_assert(NQB * (TS - 1) * CS * SLOT * 4 <= NBUF * G::STAGE, "merge slots fit the ring");
-        float *slots = (float *)s_ring;
+        // (max, sum) per share: [NQB][CS][TS][2][32]; blocks: [NQB][CS][DBW]
+        // [TS - 1 sources][32 rows][OST], rows padded to 36 floats so that the
+        // 16-byte accesses of 16 lanes fall on distinct banks
+        constexpr int OST = 36;
+        constexpr int BLK = 32 * OST;
+        constexpr int ML = NQB * CS * TS * 64;
+        static_assert((ML + NQB * CS * DBW * (TS - 1) * BLK) * 4 <= NBUF * G::STAGE, "merge slots fit the ring");
+        float *ml = (float *)s_ring + (qbw * CS + cs) * TS * 64;
+        float *ob = (float *)s_ring + ML + (qbw * CS + cs) * DBW * (TS - 1) * BLK;
         lds_barrier();
-        if (ts > 0) {
-            float *sl = slots + ((qbw * (TS - 1) + ts - 1) * CS + cs) * SLOT;
-            if (half == 0) {
-                sl[l32] = m_ref;
-                sl[32 + l32] = lrow;
-            }
+        if (half == 0) {
+            ml[ts * 64 + l32] = m_ref;
+            ml[ts * 64 + 32 + l32] = lrow;
+        }
 #pragma unroll
-            for (int db = 0; db < DBW; ++db)
+        for (int db = 0; db < DBW; ++db) {
+            const int owner = db % TS;
+            if (owner != ts) {  // source slot of this share in the owner's list
+                float *dst = ob + (db * (TS - 1) + (ts < owner ? ts : ts - 1)) * BLK + l32 * OST + 4 * half;
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4)
-                    *(f32x4_t *)(sl + 64 + l32 * OST + db * 32 + 8 * g4 + 4 * half) =
+                    *(f32x4_t *)(dst + 8 * g4) =
                         f32x4_t{oacc[db][4 * g4], oacc[db][4 * g4 + 1], oacc[db][4 * g4 + 2], oacc[db][4 * g4 + 3]};
+            }
         }
         lds_barrier();
-        if (ts == 0) {
-            float mk[TS - 1], mx = m_ref;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < TS; ++k)
+            mx = fmaxf(mx, ml[k * 64 + l32]);
+        float lsum = 0.0f;
+#pragma unroll
+        for (int k = 0; k < TS; ++k)
+            lsum += __builtin_amdgcn_exp2f(ml[k * 64 + l32] - mx) * ml[k * 64 + 32 + l32];
+        // weights of this wave's share and of the other shares, in slot order
+        const float a_own = __builtin_amdgcn_exp2f(m_ref - mx);
+        float a_src[TS - 1];
+#pragma unroll
+        for (int k = 0; k < TS - 1; ++k)
+            a_src[k] = __builtin_amdgcn_exp2f(ml[(k < ts ? k : k + 1) * 64 + l32] - mx);
+#pragma unroll
+        for (int db = 0; db < DBW; ++db) {
+            if (db % TS != ts)
+                continue;
+            oacc[db] *= a_own;
 #pragma unroll
             for (int k = 0; k < TS - 1; ++k) {
-                mk[k] = slots[((qbw * (TS - 1) + k) * CS + cs) * SLOT + l32];
-                mx = fmaxf(mx, mk[k]);
+                const float *src = ob + (db * (TS - 1) + k) * BLK + l32 * OST + 4 * half;
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const f32x4_t o = *(const f32x4_t *)(src + 8 * g4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        oacc[db][4 * g4 + e] += a_src[k] * o[e];
+                }
             }
-            const float a0 = __builtin_amdgcn_exp2f(m_ref - mx);
-            lrow *= a0;
-#pragma unroll
-            for (int db = 0; db < DBW; ++db)
-                oacc[db] *= a0;
-#pragma unroll
-            for (int k = 0; k < TS - 1; ++k) {
-                const float *sl = slots + ((qbw * (TS - 1) + k) * CS + cs) * SLOT;
-                const float ak = __builtin_amdgcn_exp2f(mk[k] - mx);
-                lrow += ak * sl[32 + l32];
-#pragma unroll
-                for (int db = 0; db < DBW; ++db)
-#pragma unroll
-                    for (int g4 = 0; g4 < 4; ++g4) {
-                        const f32x4_t o = *(const f32x4_t *)(sl + 64 + l32 * OST + db * 32 + 8 * g4 + 4 * half);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            oacc[db][4 * g4 + e] += ak * o[e];
-                    }
-            }
-            m_ref = mx;
         }
+        lrow = lsum;
+        m_ref = mx;
     }
 
-    // ---- epilogue: normalised, v_scale-multiplied partial (bf16) and its lse ----
+    // ---- epilogue: normalised, v_scale-multiplied partial (bf16) and its lse;
+    // each wave stores the column blocks it owns ----
     const int r = row0 + qbw * 32 + l32;
-    if (ts == 0 && r < rows) {
+    if (r < rows) {
         const float inv = p.v_scale / lrow;
 #pragma unroll
-        for (int db = 0; db < DBW; ++db)
+        for (int db = 0; db < DBW; ++db) {
+            if (db % TS != ts)
+                continue;
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
                 const int dv = cs * DWV + db * 32 + 8 * g4 + 4 * half;
@@ -774,7 +790,8 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64, 2) void prefix_kernel(
                                    pack_bf16x2(oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv)};
                 *(u32x2_t *)(po + (int64_t)r * D + dv) = o;
             }
-        if (cs == 0 && half == 0)
+        }
+        if (ts == 0 && cs == 0 && half == 0)
             pl[r] = (m_ref + __log2f(lrow)) * kLn2;
     }
 }

@@ -162,6 +162,21 @@ def test_fp8_head_dims(va, d):
     check_full(va, p)
 
 
+@pytest.mark.parametrize("rows", [16, 64])
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_every_prefix_kernel_shape(va, kv, d, rows):
+    # each (pool dtype, head dim, query blocks) instance of the prefix pass:
+    # 16 query rows per KV head fill one 32-row block, 64 rows two; the
+    # shapes whose tiles hold several 32-token sub-tiles merge per-wave
+    # token shares at the end of a range
+    hq, hkv, l_ext = (8, 2, 4) if rows == 16 else (8, 1, 8)
+    dt = torch.float8_e4m3fn if kv == "fp8" else torch.bfloat16
+    p = W.make_problem([300, 1000, 77], l_ext, hq, hkv, d, kv_dtype=dt, pool_factor=2, permute=True,
+                       seed=58, name="%s d%d rows %d" % (kv, d, rows))
+    check_full(va, p)
+
+
 def test_many_rows_two_row_chunks(va):
     # G=16, l_ext=8: 128 query rows per KV head -> two 64-row chunks
     check_full(va, W.make_problem([700, 1500], 8, 16, 1, 128, seed=57, name="128 rows"))
