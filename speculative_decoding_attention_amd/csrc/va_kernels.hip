@@ -41,6 +41,82 @@ typedef int i32x8_t __attribute__((ext_vector_type(8)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// ------------------------------------------------------- cross-lane steps ---
+// Reductions and scans over the 64 lanes of a wave without LDS round trips:
+// DPP row permutations inside each 16-lane row (quad_perm, row_shr,
+// row_half_mirror, row_mirror), then v_readlane of one lane per row for what
+// crosses rows.  A lane whose DPP source lies outside its row reads 0 (the
+// old value, with bound_ctrl off).
+enum : int {
+    kDppQuadXor1 = 0xB1,       // quad_perm [1,0,3,2]: lane ^ 1
+    kDppQuadXor2 = 0x4E,       // quad_perm [2,3,0,1]: lane ^ 2
+    kDppRowShr1 = 0x111,       // row_shr:1
+    kDppRowShr2 = 0x112,
+    kDppRowShr4 = 0x114,
+    kDppRowShr8 = 0x118,
+    kDppRowMirror = 0x140,     // lane 15 - i of the row
+    kDppRowHalfMirror = 0x141  // lane 7 - i of the half row
+};
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x)
+{
+    return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xf, 0xf, false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x)
+{
+    return __int_as_float(dpp_i<CTRL>(__float_as_int(x)));
+}
+
+// value of lane `l` (wave-uniform l) in every lane
+__device__ __forceinline__ int lane_i(int x, int l) { return __builtin_amdgcn_readlane(x, l); }
+__device__ __forceinline__ float lane_f(float x, int l)
+{
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+
+// sum / max over the 64 lanes, the same value in every lane
+__device__ __forceinline__ float wave_sum(float x)
+{
+    x += dpp_f<kDppQuadXor1>(x);
+    x += dpp_f<kDppQuadXor2>(x);
+    x += dpp_f<kDppRowHalfMirror>(x);
+    x += dpp_f<kDppRowMirror>(x);  // every lane holds its row's sum
+    return (lane_f(x, 0) + lane_f(x, 16)) + (lane_f(x, 32) + lane_f(x, 48));
+}
+
+__device__ __forceinline__ float wave_max(float x)
+{
+    x = fmaxf(x, dpp_f<kDppQuadXor1>(x));
+    x = fmaxf(x, dpp_f<kDppQuadXor2>(x));
+    x = fmaxf(x, dpp_f<kDppRowHalfMirror>(x));
+    x = fmaxf(x, dpp_f<kDppRowMirror>(x));
+    return fmaxf(fmaxf(lane_f(x, 0), lane_f(x, 16)), fmaxf(lane_f(x, 32), lane_f(x, 48)));
+}
+
+__device__ __forceinline__ int wave_sum_i(int x)
+{
+    x += dpp_i<kDppQuadXor1>(x);
+    x += dpp_i<kDppQuadXor2>(x);
+    x += dpp_i<kDppRowHalfMirror>(x);
+    x += dpp_i<kDppRowMirror>(x);
+    return (lane_i(x, 0) + lane_i(x, 16)) + (lane_i(x, 32) + lane_i(x, 48));
+}
+
+// inclusive prefix sum over the lanes
+__device__ __forceinline__ int wave_scan_incl(int x)
+{
+    x += dpp_i<kDppRowShr1>(x);
+    x += dpp_i<kDppRowShr2>(x);
+    x += dpp_i<kDppRowShr4>(x);
+    x += dpp_i<kDppRowShr8>(x);  // prefix within the row
+    const int t0 = lane_i(x, 15), t1 = lane_i(x, 31), t2 = lane_i(x, 47);
+    const int lane = threadIdx.x & 63;
+    return x + (lane >= 16 ? t0 : 0) + (lane >= 32 ? t1 : 0) + (lane >= 48 ? t2 : 0);
+}
+
 // ------------------------------------------------------------ conversions ---
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
 {
@@ -129,25 +205,19 @@ __device__ __forceinline__ Range locate_range(const int32_t *kv_indptr, const in
         const int32_t b = b0 + lane;
         const int32_t n = b < bs ? c.k1 - c.k0 : 0;
         const int32_t nch = (n + split_tokens - 1) / split_tokens;
-        int32_t incl = nch;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const int32_t y = __shfl_up(incl, off);
-            if (lane >= off)
-                incl += y;
-        }
-        const int32_t total = __shfl(incl, 63);
+        const int32_t incl = wave_scan_incl(nch);
+        const int32_t total = lane_i(incl, 63);
         if (cidx < cum + total) {
             const uint64_t hit = __ballot(cum + incl > cidx);
-            const int first_hit = __ffsll((unsigned long long)hit) - 1;
-            const int32_t excl = __shfl(incl - nch, first_hit);
-            const int32_t nf = __shfl(n, first_hit);
+            const int first_hit = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)hit) - 1);
+            const int32_t excl = lane_i(incl - nch, first_hit);
+            const int32_t nf = lane_i(n, first_hit);
             const int32_t ci = (int32_t)(cidx - cum - excl);
             r.b = b0 + first_hit;
             r.start = ci * split_tokens;
             r.end = min(r.start + split_tokens, nf);
-            r.kv_base = __shfl(c.k0, first_hit);
-            r.qo = __shfl(c.q0, first_hit);
+            r.kv_base = lane_i(c.k0, first_hit);
+            r.qo = lane_i(c.q0, first_hit);
             r.valid = true;
             return r;
         }
@@ -174,14 +244,10 @@ __device__ __forceinline__ void ranges_of(const int32_t *kv_indptr, const int32_
         const int32_t bb = b0 + lane;
         const int32_t nch = (c.k1 - c.k0 + split_tokens - 1) / split_tokens;
         own = bb == b ? nch : own;
-        int32_t before = bb < b ? nch : 0;
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1)
-            before += __shfl_xor(before, off);
-        acc += before;
+        acc += wave_sum_i(bb < b ? nch : 0);
     }
     *base = acc;
-    *count = __shfl(own, b & 63);
+    *count = lane_i(own, __builtin_amdgcn_readfirstlane(b & 63));
 }
 
 // ----------------------------------------------------------- prefix kernel ---
@@ -823,22 +889,6 @@ __device__ __forceinline__ void load_bf16_row(const uint16_t *src, float (&dst)[
     }
 }
 
-__device__ __forceinline__ float wave_sum(float x)
-{
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1)
-        x += __shfl_xor(x, off);
-    return x;
-}
-
-__device__ __forceinline__ float wave_max(float x)
-{
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1)
-        x = fmaxf(x, __shfl_xor(x, off));
-    return x;
-}
-
 template <int D>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     const int32_t *kv_indptr, const int32_t *qo_indptr, int32_t bs, int32_t mode, int32_t split_tokens,
@@ -927,13 +977,14 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
         den = wave_sum(e);
         // ranges in batches of PRE: every load of a batch is issued before
         // any is used; lanes hold the log-sum-exps of 64 ranges at a time
-        float lse_c = lse0;
+        // lane l holds the weight of range (s0 & ~63) + l (0 past count)
+        float w_c = lane < count ? __expf(lse0 - m) : 0.0f;
         for (int s0 = 0; s0 < count; s0 += PRE) {
             if (s0 > 0) {
                 if ((s0 & 63) == 0) {
                     const int sl = s0 + lane;
-                    lse_c = lse_row[(sl < count ? sl : last) * lse_step];
-                    lse_c = sl < count ? lse_c : -INFINITY;
+                    const float lse_c = lse_row[(sl < count ? sl : last) * lse_step];
+                    w_c = sl < count ? __expf(lse_c - m) : 0.0f;
                 }
 #pragma unroll
                 for (int i = 0; i < PRE; ++i)
@@ -941,7 +992,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
             }
 #pragma unroll
             for (int i = 0; i < PRE; ++i) {
-                const float w = __expf(__shfl(lse_c, (s0 & 63) + i) - m);  // 0 past count
+                const float w = lane_f(w_c, (s0 & 63) + i);
 #pragma unroll
                 for (int v = 0; v < VPL; ++v)
                     acc[v] += w * ov[i][v];
@@ -960,10 +1011,8 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
         sj[j] = dot;
     }
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1)
-#pragma unroll
-        for (int j = 0; j < PRE_D; ++j)
-            sj[j] += __shfl_xor(sj[j], off);
+    for (int j = 0; j < PRE_D; ++j)
+        sj[j] = wave_sum(sj[j]);
     float md = -INFINITY;
 #pragma unroll
     for (int j = 0; j < PRE_D; ++j) {
@@ -1018,9 +1067,16 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     const float tot = wp * den + wd * dd;
     const float inv = tot > 0.0f ? 1.0f / tot : 0.0f;
     uint16_t *orow = p.out + (int64_t)(qo + di) * p.o_s0 + (int64_t)h * p.o_s1 + d0;
+    uint32_t ob[VPL];
 #pragma unroll
     for (int v = 0; v < VPL; ++v)
-        orow[v] = (uint16_t)f32_to_bf16_rne((wp * acc[v] + wd * od[v]) * inv);
+        ob[v] = f32_to_bf16_rne((wp * acc[v] + wd * od[v]) * inv);
+    if constexpr (VPL == 4)
+        *(u32x2_t *)orow = u32x2_t{ob[0] | (ob[1] << 16), ob[2] | (ob[3] << 16)};
+    else if constexpr (VPL == 2)
+        *(uint32_t *)orow = ob[0] | (ob[1] << 16);
+    else
+        orow[0] = (uint16_t)ob[0];
 }
 
 // ----------------------------------------------------------------- launch ---
