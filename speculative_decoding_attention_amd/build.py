@@ -20,13 +20,14 @@ LIB_PATH = os.path.join(PKG, LIB_NAME)
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU forms.
-# kernarg preload: the first 8 kernel arguments of every kernel (the pointers
-# and sizes the range lookup needs) arrive in SGPRs at wave launch.
+# kernarg preload: the leading kernel arguments of every kernel (up to 13
+# SGPRs: the pointers and sizes the first memory round needs) arrive in SGPRs
+# at wave launch.
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall",
           "-I", INCLUDE, "-I", CSRC]
 DEVICE = ["-x", "hip", "--offload-arch=" + ARCH,
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          "-mllvm", "-amdgpu-kernarg-preload-count=8"]
+          "-mllvm", "-amdgpu-kernarg-preload-count=10"]
 
 SOURCES = ["va_kernels.hip", "va_aux.hip", "va_plan.cpp", "va_api.cpp", "va_aux_api.cpp"]
 

@@ -102,6 +102,7 @@ int prefix_impl(const void *q, const void *k_buf, const void *v_buf, const int32
     p.mode = plan.mode;
     p.split_tokens = plan.split_tokens > 0 ? plan.split_tokens : 1;
     p.n_splits = plan.n_splits > 0 ? plan.n_splits : 1;
+    p.total_tokens = (int32_t)desc->num_kv_indices;  // < 2^31, checked by the planner
     const int qb = query_blocks_for(plan.rows < kRowChunk ? plan.rows : kRowChunk);
     int e = launch_prefix(p, desc->head_dim, desc->kv_dtype == VA_DTYPE_FP8_E4M3FN, qb,
                           plan.prefix_blocks, stream);
@@ -145,6 +146,7 @@ int combine_impl(const void *q, const void *k_ext, const void *v_ext, const int3
     c.mode = plan.mode;
     c.split_tokens = plan.split_tokens > 0 ? plan.split_tokens : 1;
     c.n_splits = plan.n_splits > 0 ? plan.n_splits : 1;
+    c.range_cap = (int32_t)plan.range_slots;
     int e = launch_combine(c, desc->head_dim, plan.combine_blocks, stream);
     if (e != 0) {
         set_error("combine kernel launch: %s", hip_error_string(e));

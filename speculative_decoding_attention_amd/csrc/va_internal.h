@@ -63,6 +63,7 @@ struct PrefixParams {
     float v_scale;
     int32_t bs, h_kv, group, l_ext, rows, row_chunks;
     int32_t mode, split_tokens, n_splits;
+    int32_t total_tokens;  // num_kv_indices
 };
 
 struct CombineParams {
@@ -80,6 +81,7 @@ struct CombineParams {
     float sm_scale;
     int32_t bs, h_kv, group, l_ext, rows;
     int32_t mode, split_tokens, n_splits;
+    int32_t range_cap;  // mode 0: ranges per KV head the prefix grid holds
 };
 
 // Threads per workgroup of the append and kv_indices kernels (va_aux.hip).

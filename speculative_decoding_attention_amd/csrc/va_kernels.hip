@@ -96,6 +96,15 @@ __device__ __forceinline__ float wave_max(float x)
     return fmaxf(fmaxf(lane_f(x, 0), lane_f(x, 16)), fmaxf(lane_f(x, 32), lane_f(x, 48)));
 }
 
+__device__ __forceinline__ int wave_max_i(int x)
+{
+    x = max(x, dpp_i<kDppQuadXor1>(x));
+    x = max(x, dpp_i<kDppQuadXor2>(x));
+    x = max(x, dpp_i<kDppRowHalfMirror>(x));
+    x = max(x, dpp_i<kDppRowMirror>(x));
+    return max(max(lane_i(x, 0), lane_i(x, 16)), max(lane_i(x, 32), lane_i(x, 48)));
+}
+
 __device__ __forceinline__ int wave_sum_i(int x)
 {
     x += dpp_i<kDppQuadXor1>(x);
@@ -103,18 +112,6 @@ __device__ __forceinline__ int wave_sum_i(int x)
     x += dpp_i<kDppRowHalfMirror>(x);
     x += dpp_i<kDppRowMirror>(x);
     return (lane_i(x, 0) + lane_i(x, 16)) + (lane_i(x, 32) + lane_i(x, 48));
-}
-
-// inclusive prefix sum over the lanes
-__device__ __forceinline__ int wave_scan_incl(int x)
-{
-    x += dpp_i<kDppRowShr1>(x);
-    x += dpp_i<kDppRowShr2>(x);
-    x += dpp_i<kDppRowShr4>(x);
-    x += dpp_i<kDppRowShr8>(x);  // prefix within the row
-    const int t0 = lane_i(x, 15), t1 = lane_i(x, 31), t2 = lane_i(x, 47);
-    const int lane = threadIdx.x & 63;
-    return x + (lane >= 16 ? t0 : 0) + (lane >= 32 ? t1 : 0) + (lane >= 48 ? t2 : 0);
 }
 
 // ------------------------------------------------------------ conversions ---
@@ -146,10 +143,13 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t 
 }
 
 // ------------------------------------------------------------ range lookup ---
-// Ranges of the batch are numbered sequence by sequence.  Mode 0: sequence b
-// owns ceil(n_b / split_tokens) ranges of split_tokens tokens (the last one
-// shorter).  Mode 1 (the pages' rule): n_splits ranges of
-// ceil(ceil(n_b / n_splits) / 32) * 32 tokens, empty past the end.
+// Ranges are numbered sequence by sequence; range r of the batch and KV head
+// h writes partial slot r * h_kv + h.  Mode 0: sequence b is cut into
+// ceil(n_b / c) ranges of c tokens (the last one shorter), c fitted on the
+// device (fitted_range_units) so that the batch never needs more ranges than
+// the grid holds.  Mode 1 (the pages' rule): sequence b owns ranges
+// b * n_splits .. + n_splits - 1 of ceil(ceil(n_b / n_splits) / 32) * 32
+// tokens, empty past the end.
 struct Range {
     int32_t b;
     int32_t start;    // token range [start, end) of sequence b's prefix
@@ -173,51 +173,118 @@ __device__ __forceinline__ SeqChunk load_seq_chunk(const int32_t *kv_indptr, con
     return SeqChunk{kv_indptr[b], kv_indptr[b + 1], qo_indptr[b]};
 }
 
-// Whole-wave lookup of range `cidx`: the sequence that owns it, its token
-// range, and that sequence's kv_indptr / qo_indptr entries.  `first` holds
-// the index pointers of sequences 0..63, loaded by the caller ahead of time.
+// Mode 1: range `cidx` -> its sequence, token range and index pointers.
 __device__ __forceinline__ Range locate_range(const int32_t *kv_indptr, const int32_t *qo_indptr,
-                                              int32_t bs, int32_t mode, int32_t split_tokens,
-                                              int32_t n_splits, int64_t cidx, const SeqChunk &first)
+                                              int32_t bs, int32_t n_splits, int64_t cidx)
 {
     Range r = {0, 0, 0, 0, 0, false};
-    if (mode == 1) {
-        const int64_t b = cidx / n_splits;
-        if (b >= bs)
-            return r;
-        const int32_t s = (int32_t)(cidx % n_splits);
-        const int32_t k0 = kv_indptr[b];
-        const int32_t n = kv_indptr[b + 1] - k0;
-        const int32_t per = ((n + n_splits - 1) / n_splits + kEvenSplitGranule - 1) /
-                            kEvenSplitGranule * kEvenSplitGranule;
-        r.b = (int32_t)b;
-        r.start = s * per;
-        r.end = min(r.start + per, n);
-        r.kv_base = k0;
-        r.qo = qo_indptr[b];
-        r.valid = true;
+    const int64_t b = cidx / n_splits;
+    if (b >= bs)
         return r;
+    const int32_t s = (int32_t)(cidx % n_splits);
+    const int32_t k0 = kv_indptr[b];
+    const int32_t n = kv_indptr[b + 1] - k0;
+    const int32_t per = ((n + n_splits - 1) / n_splits + kEvenSplitGranule - 1) /
+                        kEvenSplitGranule * kEvenSplitGranule;
+    r.b = (int32_t)b;
+    r.start = s * per;
+    r.end = min(r.start + per, n);
+    r.kv_base = k0;
+    r.qo = qo_indptr[b];
+    r.valid = true;
+    return r;
+}
+
+// Mode 0 range size.  Sequence b of n_b tokens gets ceil(n_b / c) ranges of c
+// tokens; c = 64 k with k the smallest integer >= split_tokens / 64 for which
+// the batch needs at most `cap` ranges (the grid's ranges per KV head and row
+// chunk; the planner makes cap >= bs, so k = max ceil(n_b / 64) always fits).
+// With m_b = ceil(n_b / 64), sequence b's range count is ceil(m_b / k).
+// Whole-wave; `first` holds sequences 0..63.
+__device__ __forceinline__ int32_t ranges_in_chunk(const SeqChunk &c, int32_t b0, int32_t bs, uint32_t k)
+{
+    const int lane = threadIdx.x & 63;
+    const uint32_t n = b0 + lane < bs ? (uint32_t)(c.k1 - c.k0) : 0u;
+    const uint32_t m = (n + 63u) >> 6;
+    return wave_sum_i((int32_t)((m + k - 1u) / k));
+}
+
+__device__ __forceinline__ int32_t fitted_range_units(const int32_t *kv_indptr, const int32_t *qo_indptr,
+                                                      int32_t bs, int32_t split_tokens, int32_t cap,
+                                                      const SeqChunk &first)
+{
+    auto count = [&](uint32_t k) {
+        int32_t t = ranges_in_chunk(first, 0, bs, k);
+        for (int32_t b0 = 64; b0 < bs; b0 += 64)
+            t += ranges_in_chunk(load_seq_chunk(kv_indptr, qo_indptr, bs, b0), b0, bs, k);
+        return t;
+    };
+    uint32_t lo = (uint32_t)split_tokens >> 6;
+    if (count(lo) <= cap)
+        return (int32_t)lo;  // every uniform batch the planner sized
+    // count(k) <= M / k + bs with M = sum m_b, so k = ceil(M / (cap - bs))
+    // fits when cap > bs; k = max m_b fits always (one range per sequence)
+    const int lane = threadIdx.x & 63;
+    int32_t msum = 0, mmax = 0;
+    for (int32_t b0 = 0; b0 < bs; b0 += 64) {
+        const SeqChunk c = b0 == 0 ? first : load_seq_chunk(kv_indptr, qo_indptr, bs, b0);
+        const int32_t n = b0 + lane < bs ? c.k1 - c.k0 : 0;
+        const int32_t m = (n + 63) >> 6;
+        msum += wave_sum_i(m);
+        mmax = max(mmax, wave_max_i(m));
     }
+    uint32_t hi = (uint32_t)mmax;
+    if (cap > bs)
+        hi = min(hi, (uint32_t)((msum + (cap - bs) - 1) / (cap - bs)));
+    hi = max(hi, lo + 1);
+    while (lo + 1 < hi) {  // count(lo) > cap >= count(hi)
+        const uint32_t mid = lo + (hi - lo) / 2;
+        if (count(mid) <= cap)
+            hi = mid;
+        else
+            lo = mid;
+    }
+    return (int32_t)hi;
+}
+
+// inclusive prefix sum over the lanes
+__device__ __forceinline__ int wave_scan_incl(int x)
+{
+    x += dpp_i<kDppRowShr1>(x);
+    x += dpp_i<kDppRowShr2>(x);
+    x += dpp_i<kDppRowShr4>(x);
+    x += dpp_i<kDppRowShr8>(x);  // prefix within the row
+    const int t0 = lane_i(x, 15), t1 = lane_i(x, 31), t2 = lane_i(x, 47);
+    const int lane = threadIdx.x & 63;
+    return x + (lane >= 16 ? t0 : 0) + (lane >= 32 ? t1 : 0) + (lane >= 48 ? t2 : 0);
+}
+
+// Mode 0: range `cidx` -> its sequence, token range and index pointers
+// (ranges numbered sequence by sequence).
+__device__ __forceinline__ Range locate_fitted_range(const int32_t *kv_indptr, const int32_t *qo_indptr,
+                                                     int32_t bs, int32_t split_tokens, int32_t cap,
+                                                     int64_t cidx, const SeqChunk &first)
+{
+    Range r = {0, 0, 0, 0, 0, false};
+    const uint32_t k = (uint32_t)fitted_range_units(kv_indptr, qo_indptr, bs, split_tokens, cap, first);
+    const int32_t c = (int32_t)(k << 6);
     const int lane = threadIdx.x & 63;
     int64_t cum = 0;
     for (int32_t b0 = 0; b0 < bs; b0 += 64) {
-        const SeqChunk c = b0 == 0 ? first : load_seq_chunk(kv_indptr, qo_indptr, bs, b0);
-        const int32_t b = b0 + lane;
-        const int32_t n = b < bs ? c.k1 - c.k0 : 0;
-        const int32_t nch = (n + split_tokens - 1) / split_tokens;
+        const SeqChunk ch = b0 == 0 ? first : load_seq_chunk(kv_indptr, qo_indptr, bs, b0);
+        const int32_t n = b0 + lane < bs ? ch.k1 - ch.k0 : 0;
+        const int32_t nch = (int32_t)((((uint32_t)n + 63u) >> 6) + k - 1u) / (int32_t)k;
         const int32_t incl = wave_scan_incl(nch);
         const int32_t total = lane_i(incl, 63);
         if (cidx < cum + total) {
             const uint64_t hit = __ballot(cum + incl > cidx);
-            const int first_hit = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)hit) - 1);
-            const int32_t excl = lane_i(incl - nch, first_hit);
-            const int32_t nf = lane_i(n, first_hit);
-            const int32_t ci = (int32_t)(cidx - cum - excl);
-            r.b = b0 + first_hit;
-            r.start = ci * split_tokens;
-            r.end = min(r.start + split_tokens, nf);
-            r.kv_base = lane_i(c.k0, first_hit);
-            r.qo = lane_i(c.q0, first_hit);
+            const int h = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)hit) - 1);
+            const int32_t ci = (int32_t)(cidx - cum - lane_i(incl - nch, h));
+            r.b = b0 + h;
+            r.start = ci * c;
+            r.end = min(r.start + c, lane_i(n, h));
+            r.kv_base = lane_i(ch.k0, h);
+            r.qo = lane_i(ch.q0, h);
             r.valid = true;
             return r;
         }
@@ -226,23 +293,24 @@ __device__ __forceinline__ Range locate_range(const int32_t *kv_indptr, const in
     return r;
 }
 
-// First range index and range count of sequence b (whole-wave call); `first`
-// holds the index pointers of sequences 0..63 (see load_seq_chunk).
+// First partial slot and slot count of sequence b (whole-wave call).
 __device__ __forceinline__ void ranges_of(const int32_t *kv_indptr, const int32_t *qo_indptr, int32_t bs,
-                                          int32_t mode, int32_t split_tokens, int32_t n_splits, int32_t b,
-                                          const SeqChunk &first, int32_t *base, int32_t *count)
+                                          int32_t mode, int32_t split_tokens, int32_t n_splits, int32_t cap,
+                                          int32_t b, const SeqChunk &first, int32_t *base, int32_t *count)
 {
     if (mode == 1) {
         *base = b * n_splits;
         *count = n_splits;
         return;
     }
+    const uint32_t k = (uint32_t)fitted_range_units(kv_indptr, qo_indptr, bs, split_tokens, cap, first);
     const int lane = threadIdx.x & 63;
     int32_t acc = 0, own = 0;
     for (int32_t b0 = 0; b0 <= b; b0 += 64) {
         const SeqChunk c = b0 == 0 ? first : load_seq_chunk(kv_indptr, qo_indptr, bs, b0);
         const int32_t bb = b0 + lane;
-        const int32_t nch = (c.k1 - c.k0 + split_tokens - 1) / split_tokens;
+        const uint32_t m = ((uint32_t)(bb < bs ? c.k1 - c.k0 : 0) + 63u) >> 6;
+        const int32_t nch = (int32_t)((m + k - 1u) / k);
         own = bb == b ? nch : own;
         acc += wave_sum_i(bb < b ? nch : 0);
     }
@@ -371,8 +439,9 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 // same fields are also in p.
 template <bool FP8, int D, int NQB>
 __global__ __launch_bounds__(prefix_waves(NQB) * 64, 2) void prefix_kernel(
-    const int32_t *kv_indptr, const int32_t *qo_indptr, int32_t bs, int32_t mode, int32_t split_tokens,
-    int32_t n_splits, int32_t h_kv, int32_t row_chunks, const PrefixParams p)
+    const int32_t *kv_indptr, const int32_t *qo_indptr, const int64_t *kv_indices, int32_t bs, int32_t mode,
+    int32_t split_tokens, int32_t total_tokens, int32_t h_kv, int32_t row_chunks, int32_t n_splits,
+    const PrefixParams p)
 {
     using G = PrefixGeom<FP8, D, NQB>;
     constexpr int NW = G::NW;
@@ -418,77 +487,35 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64, 2) void prefix_kernel(
     const int half = lane >> 5;  // k half of the operands
 
     // ---- work item: (range, KV head, row chunk) ----
-    // index pointers of the first 64 sequences, then the remaining kernel
-    // arguments while those loads are in flight
-    const SeqChunk first = load_seq_chunk(kv_indptr, qo_indptr, bs, 0);
-    asm volatile("" ::"s"(p.q), "s"(p.kv_indices), "s"(p.k_buf), "s"(p.v_buf), "s"(p.kb_s1), "s"(p.vb_s1),
-                 "s"(p.kb_s0), "s"(p.vb_s0), "s"(p.q_s0), "s"(p.q_s1), "s"(p.group), "s"(p.l_ext), "s"(p.rows)
-                 : "memory");
     const uint32_t blk = blockIdx.x;
     const int rc = (int)(blk % (uint32_t)row_chunks);
     const uint32_t t1 = blk / (uint32_t)row_chunks;
     const int kvh = (int)(t1 % (uint32_t)h_kv);
     const int64_t cidx = t1 / (uint32_t)h_kv;
-    const Range rg = locate_range(kv_indptr, qo_indptr, bs, mode, split_tokens, n_splits, cidx, first);
-    if (!rg.valid)
-        return;  // surplus slot of the static grid: never read by the combine pass
-    const int64_t slot = cidx * h_kv + kvh;
-    const int rows = p.rows;
     const int row0 = rc * kRowChunk;
-    uint16_t *po = p.part_o + slot * (int64_t)rows * D;
-    float *pl = p.part_lse + slot * (int64_t)rows;
-
-    if (rg.start >= rg.end) {
-        // Empty range: output 0 and log-sum-exp -inf, so the merge weight is
-        // exactly 0 and no stale value can leak in.
-        const int nr = min(rows - row0, NQB * 32);
-        for (int e = tid; e < nr * D; e += NW * 64)
-            po[(int64_t)(row0 + e / D) * D + (e % D)] = 0;
-        if (tid < nr)
-            pl[row0 + tid] = -INFINITY;
-        return;
-    }
-
-    const int64_t kv0 = (int64_t)rg.kv_base + rg.start;
-    const int len = rg.end - rg.start;
-    const int nt = (len + TN - 1) / TN;
-    const int qo = rg.qo;
     const uint32_t ring = lds_offset(s_ring);
-
-    // ---- query tile -> ring stage NBUF-1 (bf16 rows of D, row-major) ----
-    constexpr int QCH = D / 8;                    // 16-byte chunks per query row
-    constexpr int QI = NQB * 32 * QCH / 64;       // wave-wide copies for the tile
-    constexpr int QPW = QI / NW;                  // of which each wave issues
-    static_assert(QI % NW == 0, "query copies split evenly over the waves");
-    auto issue_query = [&]() {
-#pragma unroll
-        for (int k = 0; k < QPW; ++k) {
-            const int i = wave + k * NW;
-            const int e = i * 64 + lane;
-            const int r = row0 + e / QCH;             // query row of this chunk
-            const int rr = r < rows ? r : row0;       // padding rows copy a valid row
-            const int hg = rr / p.l_ext, di = rr % p.l_ext;
-            const uint16_t *src = p.q + (int64_t)(qo + di) * p.q_s0 +
-                                  (int64_t)(kvh * p.group + hg) * p.q_s1 + (e % QCH) * 8;
-            dma16(src, __builtin_amdgcn_readfirstlane(ring + (NBUF - 1) * G::STAGE + i * 1024));
-        }
-    };
-
-    // ---- copy issue: index slots and K/V tiles ----
     const uint32_t idx_base = lds_offset(&s_idx[wave][0][0]);
+    const bool paged = kv_indices == nullptr;  // prefix rows through a page table
+
+    // The piece being processed: tokens [pstart, pstart + len) of sequence pb,
+    // whose first token sits at kv_indices position kv0.  Index entries
+    // kv0 .. kv0 + fetch - 1 may be read (fetch >= len); tokens past len are
+    // masked out of the scores and their K/V copies read pool row 0.
+    int64_t kv0 = 0;
+    int len = 0, fetch = 1, pb = 0, pstart = 0, qo = 0;
+
+    // ---- copy issue: index slots, K/V tiles, query tile ----
     auto issue_idx = [&](int k) {
-        // rows wave*RW .. +RW of tile k; tokens past the range re-read the last
-        // token (in bounds, and masked out of the scores)
+        // rows wave*RW .. +RW of tile k: the two dwords of the int64 index, or
+        // the token's page id in both lanes of the pair
         if (lane < 2 * RW) {
             int tok = k * TN + wave * RW + (lane >> 1);
-            tok = tok < len ? tok : len - 1;
-            // token rows: the two dwords of the int64 index; page table: both
-            // lanes of the pair fetch the token's page id
-            const uint32_t *src =
-                p.block_table
-                    ? (const uint32_t *)(p.block_table + (int64_t)rg.b * p.bt_s0 + (rg.start + tok) / p.page_size)
-                    : (const uint32_t *)(p.kv_indices + kv0 + tok) + (lane & 1);
-            dma4(src, __builtin_amdgcn_readfirstlane(idx_base + (k % G::NIDX) * RW * 8));
+            tok = tok < fetch ? tok : fetch - 1;
+            const uint32_t dst = __builtin_amdgcn_readfirstlane(idx_base + (k % G::NIDX) * RW * 8);
+            if (paged)
+                dma4(p.block_table + (int64_t)pb * p.bt_s0 + (pstart + tok) / p.page_size, dst);
+            else
+                dma4((const uint32_t *)(kv_indices + kv0 + tok) + (lane & 1), dst);
         }
     };
     const uint8_t *kbase = p.k_buf + (int64_t)kvh * p.kb_s1;
@@ -502,51 +529,136 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64, 2) void prefix_kernel(
             const int row = wave * RW + rl;           // row within the tile
             const int pc = lane % LCH;                // LDS chunk within the row
             const int vz = vswz(row);
+            const int tok = k * TN + row;
             uint64_t t = (uint64_t)ix[rl];
-            if (p.block_table) {  // pool row = page id * page_size + position in the page
-                int tok = k * TN + row;
-                tok = tok < len ? tok : len - 1;
-                t = (uint64_t)(uint32_t)t * (uint32_t)p.page_size + (uint32_t)((rg.start + tok) % p.page_size);
-            }
+            if (paged)  // pool row = page id * page_size + position in the page
+                t = (uint64_t)(uint32_t)t * (uint32_t)p.page_size + (uint32_t)((pstart + tok) % p.page_size);
+            t = tok < len ? t : 0;
             dma16(kbase + t * p.kb_s0 + ((pc ^ kswz(row)) << 4),
                   __builtin_amdgcn_readfirstlane(st + i * 1024));
             dma16(vbase + t * p.vb_s0 + ((pc ^ vz) << 4),
                   __builtin_amdgcn_readfirstlane(st + G::STAGE_K + i * 1024));
         }
     };
+    // query tile -> ring stage NBUF-1 (bf16 rows of D, row-major)
+    constexpr int QCH = D / 8;                    // 16-byte chunks per query row
+    constexpr int QI = NQB * 32 * QCH / 64;       // wave-wide copies for the tile
+    constexpr int QPW = QI / NW;                  // of which each wave issues
+    static_assert(QI % NW == 0, "query copies split evenly over the waves");
+    auto issue_query = [&]() {
+        const int rows = p.rows;
+#pragma unroll
+        for (int k = 0; k < QPW; ++k) {
+            const int i = wave + k * NW;
+            const int e = i * 64 + lane;
+            const int r = row0 + e / QCH;             // query row of this chunk
+            const int rr = r < rows ? r : row0;       // padding rows copy a valid row
+            const int hg = rr / p.l_ext, di = rr % p.l_ext;
+            const uint16_t *src = p.q + (int64_t)(qo + di) * p.q_s0 +
+                                  (int64_t)(kvh * p.group + hg) * p.q_s1 + (e % QCH) * 8;
+            dma16(src, __builtin_amdgcn_readfirstlane(ring + (NBUF - 1) * G::STAGE + i * 1024));
+        }
+    };
 
-    // prologue: steps j = 0 .. NBUF-2, step j = [index copy of tile j+2][tile j].
-    // Loads retire in order, so "index slot j has landed" is "at most the
-    // loads issued after it are outstanding".  Index slot 0 goes out ahead of
-    // the query tile, so tile 0 waits only for its indices; the query tile is
-    // awaited just before the first tile.
+    // ---- range ----
+    // Mode 0: every prefix is cut into ranges of c tokens (the last one of a
+    // sequence shorter), c the smallest multiple of 64 that is at least
+    // split_tokens and gives no more ranges than the grid holds.  When every
+    // prefix is a multiple of split_tokens, range cidx starts at kv_indices
+    // position cidx * split_tokens: its first three index copies go out before
+    // the index pointers are read, and are used if the range really starts
+    // there.  Mode 1 (the pages' rule): range cidx is split cidx % n_splits of
+    // sequence cidx / n_splits.
+    const SeqChunk first = load_seq_chunk(kv_indptr, qo_indptr, bs, 0);
+    int64_t P0 = -1;
+    int early_fetch = 0;
+    if (mode == 0 && !paged) {
+        const int64_t g0 = cidx * (int64_t)split_tokens;
+        if (g0 < total_tokens) {
+            P0 = g0;
+            kv0 = g0;
+            fetch = (int)min((int64_t)split_tokens, (int64_t)total_tokens - g0);
+            early_fetch = fetch;
+            issue_idx(0);
+            issue_idx(1);
+            issue_idx(2);
+        }
+    }
+    // the remaining kernel arguments while those loads are in flight (the
+    // scheduling barrier keeps the early copies ahead of their wait; row_chunks
+    // stays live so that no register of the argument loads is reused early)
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::"s"(p.q), "s"(p.k_buf), "s"(p.v_buf), "s"(p.kb_s1), "s"(p.vb_s1), "s"(p.kb_s0),
+                 "s"(p.vb_s0), "s"(p.q_s0), "s"(p.q_s1), "s"(p.group), "s"(p.l_ext), "s"(p.rows),
+                 "s"(p.row_chunks)
+                 : "memory");
+    const int rows = p.rows;
+    const int32_t range_cap = (int32_t)(gridDim.x / (uint32_t)(h_kv * row_chunks));  // ranges per (KV head, chunk)
+    const Range rg = mode == 0 ? locate_fitted_range(kv_indptr, qo_indptr, bs, split_tokens, range_cap, cidx, first)
+                               : locate_range(kv_indptr, qo_indptr, bs, n_splits, cidx);
+    if (!rg.valid) {
+        wait_vm<0>();  // early index copies of a surplus slot of the static grid
+        return;        // (never read by the combine pass)
+    }
+    const int64_t slot = cidx * h_kv + kvh;
+    uint16_t *po = p.part_o + slot * (int64_t)rows * D;
+    float *pl = p.part_lse + slot * (int64_t)rows;
+    if (rg.start >= rg.end) {
+        // Empty range (mode 1 past the end): output 0 and log-sum-exp -inf, so
+        // the merge weight is exactly 0 and no stale value can leak in.
+        const int nr = min(rows - row0, NQB * 32);
+        for (int e = tid; e < nr * D; e += NW * 64)
+            po[(int64_t)(row0 + e / D) * D + (e % D)] = 0;
+        if (tid < nr)
+            pl[row0 + tid] = -INFINITY;
+        return;
+    }
+    pb = rg.b;
+    pstart = rg.start;
+    len = rg.end - rg.start;
+    fetch = len;
+    kv0 = (int64_t)rg.kv_base + rg.start;
+    qo = rg.qo;
+    // the early index copies are this range's if it starts at P0 and they
+    // cover every token of tiles 0..2
+    const bool ready = kv0 == P0 && min(len, 3 * TN) <= early_fetch;
+    const int nt = (len + TN - 1) / TN;
+
+
+    // prologue: index slots 0..2, the query tile, then steps
+    // j = 0 .. NBUF-2, step j = [tile j][index copy of tile j+2].  Loads
+    // retire in order, so "slot j has landed" is "at most the loads issued
+    // after it are outstanding" (loads between them that were already
+    // awaited only make a wait stricter).
     static_assert(NBUF == 2 || NBUF == 4, "wait counts are written for 2- or 4-stage rings");
-    issue_idx(0);
+    if (!ready) {
+        issue_idx(0);
+        issue_idx(1);
+        issue_idx(2);
+    }
     issue_query();
-    issue_idx(1);
-    issue_idx(2);
-    wait_vm<QPW + 2>();  // index slot 0: the query copies and 2 index copies came after it
+    wait_vm<QPW + 2>();  // index slot 0: then slots 1, 2 and the query copies
     issue_tile(0);
     if constexpr (NBUF == 4) {
         issue_idx(3);
         if (1 < nt) {
-            wait_vm<2 * NIKW + 2>();  // index slot 1: then slot 2, tile 0, slot 3
+            wait_vm<QPW + 2 * NIKW + 2>();  // index slot 1: then slot 2, query, tile 0, slot 3
             issue_tile(1);
         }
         issue_idx(4);
         if (2 < nt) {
-            wait_vm<4 * NIKW + 2>();  // index slot 2: then tile 0, slot 3, tile 1, slot 4
+            wait_vm<QPW + 4 * NIKW + 2>();  // index slot 2: then query, tile 0, slot 3, tile 1, slot 4
             issue_tile(2);
         }
-        // after the query tile: index slots 1..4 and min(nt, 3) tiles
+        // the query tile: then min(nt, 3) tiles and index slots 3, 4
         if (nt >= 3)
-            wait_vm<4 + 6 * NIKW>();
+            wait_vm<2 + 6 * NIKW>();
         else if (nt == 2)
-            wait_vm<4 + 4 * NIKW>();
+            wait_vm<2 + 4 * NIKW>();
         else
-            wait_vm<4 + 2 * NIKW>();
+            wait_vm<2 + 2 * NIKW>();
     } else {
-        wait_vm<2 + 2 * NIKW>();  // after the query tile: index slots 1, 2 and tile 0
+        wait_vm<2 * NIKW>();  // the query tile: then tile 0
     }
     lds_barrier();
 
@@ -916,10 +1028,11 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     const int qo = qo_indptr[b];
     const SeqChunk first = load_seq_chunk(kv_indptr, qo_indptr, bs, 0);
     asm volatile("" ::"s"(p.q), "s"(p.k_ext), "s"(p.v_ext), "s"(p.part_o), "s"(p.part_lse), "s"(p.q_s0),
-                 "s"(p.q_s1), "s"(p.ke_s0), "s"(p.ke_s1), "s"(p.ve_s0), "s"(p.ve_s1), "s"(p.group), "s"(p.l_ext)
+                 "s"(p.q_s1), "s"(p.ke_s0), "s"(p.ke_s1), "s"(p.ve_s0), "s"(p.ve_s1), "s"(p.group), "s"(p.l_ext),
+                 "s"(p.range_cap)
                  : "memory");
     int32_t base, count;
-    ranges_of(kv_indptr, qo_indptr, bs, mode, split_tokens, n_splits, b, first, &base, &count);
+    ranges_of(kv_indptr, qo_indptr, bs, mode, split_tokens, n_splits, p.range_cap, b, first, &base, &count);
     const int L = p.l_ext;
     int64_t mrow = 0;  // this row's tree-mask bytes for the draft keys
     if (p.mask)
@@ -1084,12 +1197,13 @@ template <bool FP8, int D>
 static int launch_prefix_qb(const PrefixParams &p, int qblocks, int64_t blocks, hipStream_t s)
 {
     dim3 grid((unsigned)blocks), block(prefix_waves(qblocks) * 64);
+#define VA_PREFIX_ARGS p.kv_indptr, p.qo_indptr, p.kv_indices, p.bs, p.mode, p.split_tokens, p.total_tokens, \
+                       p.h_kv, p.row_chunks, p.n_splits, p
     if (qblocks == 1)
-        hipLaunchKernelGGL((prefix_kernel<FP8, D, 1>), grid, block, 0, s, p.kv_indptr, p.qo_indptr, p.bs, p.mode,
-                           p.split_tokens, p.n_splits, p.h_kv, p.row_chunks, p);
+        hipLaunchKernelGGL((prefix_kernel<FP8, D, 1>), grid, block, 0, s, VA_PREFIX_ARGS);
     else
-        hipLaunchKernelGGL((prefix_kernel<FP8, D, 2>), grid, block, 0, s, p.kv_indptr, p.qo_indptr, p.bs, p.mode,
-                           p.split_tokens, p.n_splits, p.h_kv, p.row_chunks, p);
+        hipLaunchKernelGGL((prefix_kernel<FP8, D, 2>), grid, block, 0, s, VA_PREFIX_ARGS);
+#undef VA_PREFIX_ARGS
     return (int)hipGetLastError();
 }
 

@@ -8,6 +8,7 @@
 // this idea: a split count from the average prefix length).
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdarg>
@@ -151,16 +152,24 @@ int make_plan(const va_desc_t *d, int32_t l_ext, int32_t num_cus, va_plan_t *pla
     p.row_chunks = (int32_t)((rows + kRowChunk - 1) / kRowChunk);
     p.tile_tokens = tile_tokens_for(d->head_dim, d->kv_dtype == VA_DTYPE_FP8_E4M3FN ? 1 : 2);
     const int64_t T = d->num_kv_indices;
+    int64_t ranges;  // prefix workgroups per (KV head, row chunk)
     if (d->n_splits > 0) {
         p.mode = 1;
         p.n_splits = d->n_splits;
-        p.range_slots = (int64_t)d->bs * d->n_splits;
+        ranges = (int64_t)d->bs * d->n_splits;
+        p.range_slots = ranges;
     } else {
         p.mode = 0;
         int64_t c = d->split_tokens;
-        if (c == 0) {
-            // Enough ranges that every CU holds its resident prefix
-            // workgroups; never fewer than kSplitQuantum tokens per range.
+        if (c > 0) {
+            // every prefix cut into ranges of exactly c tokens:
+            // sum_b ceil(n_b / c) <= floor((T + bs * (c - 1)) / c)
+            ranges = (T + (int64_t)d->bs * (c - 1)) / c;
+        } else {
+            // As many ranges as the CUs hold resident prefix workgroups,
+            // never fewer than kSplitQuantum tokens each.  The kernels grow
+            // the range size on the device (in steps of kSplitQuantum) until a
+            // ragged batch fits this count, one range per sequence at least.
             const int64_t units = (int64_t)d->h_kv * p.row_chunks;
             const int qb = query_blocks_for(rows < kRowChunk ? (int)rows : kRowChunk);
             const int64_t target = (int64_t)prefix_resident_per_cu(qb) * num_cus;
@@ -168,13 +177,13 @@ int make_plan(const va_desc_t *d, int32_t l_ext, int32_t num_cus, va_plan_t *pla
             c = align_up(c < kSplitQuantum ? kSplitQuantum : c, kSplitQuantum);
             if (c > (1 << 30))
                 c = 1 << 30;
+            ranges = T > 0 ? std::max<int64_t>((T + c - 1) / c, d->bs) : 0;
         }
         p.split_tokens = (int32_t)c;
-        // sum_b ceil(n_b / c) <= floor((T + bs * (c - 1)) / c)
-        p.range_slots = (T + (int64_t)d->bs * (c - 1)) / c;
+        p.range_slots = ranges;
     }
     const int64_t slots = p.range_slots * d->h_kv;
-    p.prefix_blocks = slots * p.row_chunks;
+    p.prefix_blocks = ranges * d->h_kv * p.row_chunks;
     // one wavefront per output row
     p.combine_blocks = ((int64_t)d->bs * d->h_kv * rows + kCombineRowsPerBlock - 1) / kCombineRowsPerBlock;
     if (p.prefix_blocks > INT32_MAX || p.combine_blocks > INT32_MAX || p.range_slots > INT32_MAX)

@@ -110,8 +110,21 @@ def test_plan_headline_shapes():
     assert plan.workspace_bytes >= plan.range_slots * 2 * 32 * (256 * 2 + 4)
 
 
+def _fitted_units(lens, split_tokens, cap):
+    """The kernels' mode-0 range size in units of 64 tokens: the smallest k >=
+    split_tokens / 64 with sum_b ceil(ceil(n_b / 64) / k) <= cap (plain search)."""
+    m = [-(-n // 64) for n in lens]
+    k = split_tokens // 64
+    while sum(-(-x // k) for x in m) > cap:
+        k += 1
+    return k
+
+
 @pytest.mark.parametrize("seed", range(5))
-def test_range_slots_bound_every_ragged_batch(seed):
+def test_ragged_batches_fit_the_resident_workgroups(seed):
+    # Mode 0 (heuristic): the grid holds as many ranges per KV head as the CUs
+    # keep resident (at least one per sequence); the kernels grow the range
+    # size until a ragged batch fits, so no workgroup waits for a second round.
     g = torch.Generator().manual_seed(seed)
     bs = int(torch.randint(1, 40, (1,), generator=g))
     lens = torch.randint(0, 5000, (bs,), generator=g).tolist()
@@ -122,7 +135,26 @@ def test_range_slots_bound_every_ragged_batch(seed):
         plan = va.verify_attn_plan(va.make_desc(**meta), 2, cus)
         c = plan.split_tokens
         assert c % 64 == 0 and c >= 64
-        assert sum(math.ceil(n / c) for n in lens) <= plan.range_slots
+        cap = plan.prefix_blocks  # one KV head, one row chunk
+        assert plan.range_slots == cap
+        if T == 0:
+            assert cap == 0
+            continue
+        assert cap == max(-(-T // c), bs)
+        assert cap <= max(2 * cus, bs, -(-T // 64))  # two resident 4-wave workgroups per CU
+        k = _fitted_units(lens, c, cap)
+        assert k * 64 <= max(c, -(-max(lens) // 64) * 64)
+        assert sum(-(-n // (64 * k)) for n in lens) <= cap
+
+
+def test_explicit_split_tokens_are_kept():
+    # split_tokens given: the grid bound covers every batch at exactly that size
+    lens = [100, 1, 4097, 64, 0, 700]
+    meta = meta_problem(bs=len(lens), l_ext=2, h_q=8, h_kv=1, d=128, n=1)
+    meta["kv_indices"] = torch.empty(sum(lens), dtype=torch.int64, device="meta")
+    plan = va.verify_attn_plan(va.make_desc(**meta, split_tokens=128), 2, 256)
+    assert plan.split_tokens == 128
+    assert _fitted_units(lens, 128, plan.range_slots) == 2
 
 
 def test_pages_split_rule_mode():

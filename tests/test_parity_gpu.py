@@ -149,6 +149,40 @@ def test_many_sequences(va, kw):
     check_full(va, p, **kw)
 
 
+def _grown_units(va, p):
+    """(host range size / 64, the kernels' fitted range size / 64) for p."""
+    out = torch.empty(p.q.shape[0], p.h_q, p.v_head_dim, dtype=torch.bfloat16, device="meta")
+    plan = va.verify_attn_plan(va.make_desc(p.q, p.k_ext, p.v_ext, p.k_buf, p.v_buf, p.kv_indices, out,
+                                            p.bs), p.l_ext)
+    lens = (p.kv_indptr[1:] - p.kv_indptr[:-1]).tolist()
+    m = [-(-n // 64) for n in lens]
+    k = plan.split_tokens // 64
+    while sum(-(-x // k) for x in m) > plan.range_slots:
+        k += 1
+    return plan.split_tokens // 64, k
+
+
+@pytest.mark.parametrize("case", ["bf16 six", "bf16 100 sequences", "fp8 four"])
+def test_fitted_range_size_grows_for_ragged_batches(va, case):
+    # Ragged batches whose per-sequence ranges at the host's size would
+    # exceed the grid: the kernels grow the range size on the device.  The
+    # first range starts where the early index copies went, but is longer
+    # than they cover, so the prefix pass must fetch its indices again.
+    if case == "bf16 six":
+        p = W.make_problem([100, 1, 4097, 64, 0, 700], 4, 16, 2, 256, pool_factor=2, permute=True,
+                           seed=81, name=case)
+    elif case == "bf16 100 sequences":
+        g = torch.Generator().manual_seed(82)
+        lens = torch.randint(0, 2000, (100,), generator=g).tolist()
+        p = W.make_problem(lens, 2, 8, 1, 256, pool_factor=2, permute=True, seed=83, name=case)
+    else:
+        p = W.make_problem([3000, 5, 129, 2049], 8, 8, 1, 128, kv_dtype=torch.float8_e4m3fn,
+                           pool_factor=2, permute=True, seed=84, name=case)
+    k_host, k_dev = _grown_units(va, p)
+    assert k_dev > k_host, "the case must make the kernels grow the range size"
+    check_full(va, p)
+
+
 def test_kv_scales(va):
     check_full(va, W.make_problem([1024, 2048], 4, 16, 2, 256, k_scale=0.5, v_scale=0.25, seed=55,
                                   name="scales"))
