@@ -13,10 +13,9 @@
  * with one softmax over both.  Query heads are grouped contiguously per KV
  * head (kv_head = h / (h_q / h_kv)).
  *
- * Execution: two kernels on the caller's stream.  The prefix pass splits the
- * prefixes into ranges processed in parallel; each range writes, for every
- * sequence it covers, a normalised partial output and its log-sum-exp into the
- * caller's workspace.
+ * Execution: two kernels on the caller's stream.  The prefix pass splits every
+ * sequence's prefix into ranges processed in parallel; each range writes a
+ * normalised partial output and its log-sum-exp into the caller's workspace.
  * The combine pass merges the ranges by log-sum-exp, computes the small causal
  * draft block and merges the two.  No call allocates, synchronises, or reads
  * device memory on the host, so every call may be captured into a HIP graph.
@@ -76,12 +75,12 @@ typedef enum {
  *   out    [q_rows, h_q,  v_head_dim]  bf16     strides out_stride[0..1]
  * num_kv_indices is the length of kv_indices (a static shape that sizes the
  * work; every kv_indptr entry must lie in [0, num_kv_indices]).
- * Splitting (both 0 = the library's static heuristic):
- *   split_tokens > 0 : kv_indices positions 0 .. num_kv_indices - 1 (the
- *                      prefixes one after another) are cut into ranges of
- *                      split_tokens positions (a multiple of 64), one work
- *                      item each; a range that spans sequence boundaries
- *                      holds one piece per sequence, processed in order;
+ * Splitting (both 0 = the library's heuristic: the grid holds one range per
+ * resident prefix workgroup, at least one per sequence, and the kernels pick
+ * the range size from kv_indptr -- the smallest multiple of 64, at least the
+ * planner's split_tokens, whose ranges fit that grid):
+ *   split_tokens > 0 : every prefix is cut into ranges of split_tokens tokens
+ *                      (a multiple of 64), one work item each;
  *   n_splits > 0     : the pages' rule -- every prefix is cut into n_splits
  *                      ranges of ceil(ceil(n_b / n_splits) / 32) * 32 tokens;
  *                      ranges past the end are empty.
@@ -109,16 +108,14 @@ typedef struct {
  * l_ext and the CU count; identical for every call with the same inputs, so a
  * workspace sized once stays valid, as graph capture needs). */
 typedef struct {
-    int32_t mode;            /* 0: fixed-size ranges of kv_indices positions; 1: n_splits equal
-                                ranges per sequence */
-    int32_t split_tokens;    /* positions per range (mode 0) */
+    int32_t mode;            /* 0: ranges of split_tokens tokens (or more, see above); 1: n_splits
+                                equal ranges per sequence */
+    int32_t split_tokens;    /* tokens per range (mode 0; the heuristic's smallest size) */
     int32_t n_splits;        /* ranges per sequence (mode 1) */
     int32_t rows;            /* query rows per KV head: (h_q / h_kv) * l_ext */
     int32_t row_chunks;      /* rows are processed in chunks of at most 64 */
     int32_t tile_tokens;     /* prefix tokens per LDS tile in the prefix kernel */
-    int64_t range_slots;     /* partial-output slots per KV head: ranges + bs - 1 in mode 0
-                                (piece of range r and sequence b -> slot r + b), bs * n_splits
-                                in mode 1 */
+    int64_t range_slots;     /* ranges (partial-output slots) per KV head the grid holds */
     int64_t prefix_blocks;   /* grid of the prefix kernel (workgroups of 256 or 512 threads) */
     int64_t combine_blocks;  /* grid of the combine kernel (one 64-thread workgroup per output row) */
     size_t workspace_bytes;  /* bytes of workspace the two passes need */
