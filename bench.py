@@ -36,7 +36,8 @@ def parse_args():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=300,
+                    help="untimed iterations of each timed loop's body right before it")
     ap.add_argument("--replicas", type=int, default=8,
                     help="independent input sets rotated through the timed loop")
     ap.add_argument("--workload", default="b8_8k")
@@ -101,13 +102,25 @@ class Runner:
             raise RuntimeError("verify_attn_combine: %d %s" % (rc, self.lib.verify_attn_last_error()))
 
 
-def hold_gpu(torch, ms=20.0):
-    """Keep the GPU busy for ~ms so the host can enqueue the timed launches
-    ahead of execution (the measured region then has no host gaps)."""
-    try:
-        torch.cuda._sleep(int(ms * 1e-3 * 2.4e9))
-    except Exception:
-        pass
+def timed_loop(torch, body, steps, warmup):
+    """ms per iteration of body(i) over `steps` iterations on the current
+    stream, right after `warmup` untimed iterations of the same body.  The
+    warm-up keeps the GPU under the same load until the timed region starts:
+    after an idle or lightly loaded gap its clocks come back over several
+    milliseconds, and the first few hundred steps would time the ramp.  The
+    host enqueues each step faster than the GPU runs it, so the stream never
+    starves inside the timed region."""
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        body(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        body(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
 
 
 def time_workload(torch, va, W, name, steps, warmup, replicas, seed0=1000):
@@ -133,33 +146,17 @@ def time_workload(torch, va, W, name, steps, warmup, replicas, seed0=1000):
         r.prefix(sh)
         r.combine(sh)
 
-    for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize()
-
     # ---- timed region: whole steps, rotating replicas (cold K/V) ----
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    hold_gpu(torch)
-    e0.record(stream)
-    for i in range(steps):
-        step(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_step = e0.elapsed_time(e1) / steps
+    ms_step = timed_loop(torch, step, steps, warmup)
 
     # ---- prefix kernel alone, back to back ----
-    hold_gpu(torch)
-    e0.record(stream)
-    for i in range(steps):
-        runners[i % replicas].prefix(sh)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_prefix_b2b = e0.elapsed_time(e1) / steps
+    ms_prefix_b2b = timed_loop(torch, lambda i: runners[i % replicas].prefix(sh), steps, warmup)
 
     # ---- per-kernel durations with events on the launch stream (the roofline's kernel time) ----
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    hold_gpu(torch)
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
     for i in range(steps):
         r = runners[i % replicas]
         ev[i][0].record(stream)
@@ -172,14 +169,10 @@ def time_workload(torch, va, W, name, steps, warmup, replicas, seed0=1000):
     com = [ev[i][1].elapsed_time(ev[i][2]) for i in range(steps)]
 
     # ---- warm cache: one replica over and over ----
-    hold_gpu(torch)
-    e0.record(stream)
-    for i in range(steps):
+    def warm_step(i):
         runners[0].prefix(sh)
         runners[0].combine(sh)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_warm = e0.elapsed_time(e1) / steps
+    ms_warm = timed_loop(torch, warm_step, steps, warmup)
 
     # ---- graph replay: one captured step per replica ----
     graphs = []
@@ -196,16 +189,7 @@ def time_workload(torch, va, W, name, steps, warmup, replicas, seed0=1000):
                 graphs.append(g)
         stream.wait_stream(cap)
         torch.cuda.synchronize()
-        for i in range(warmup):
-            graphs[i % replicas].replay()
-        torch.cuda.synchronize()
-        hold_gpu(torch)
-        e0.record(stream)
-        for i in range(steps):
-            graphs[i % replicas].replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms_graph = e0.elapsed_time(e1) / steps
+        ms_graph = timed_loop(torch, lambda i: graphs[i % replicas].replay(), steps, warmup)
     except Exception as exc:  # report, never hide
         ms_graph = None
         print("graph replay timing failed: %r" % (exc,), file=sys.stderr)
@@ -240,14 +224,20 @@ def calibration_copy(torch):
 
 
 def _time_calls(torch, fn, steps, warmup):
-    """Mean µs of fn(i) over `steps` calls enqueued behind a GPU hold, events
-    on the current stream."""
+    """Mean µs of fn(i) over `steps` calls through the Python binding, right
+    after `warmup` untimed calls.  These calls marshal their arguments on the
+    host each time, which takes about as long as a small kernel runs, so a
+    short spin kernel (sized to the host's enqueue time for the timed calls)
+    lets the host get ahead before the timed region starts."""
     stream = torch.cuda.current_stream()
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    hold_gpu(torch)
+    try:
+        torch.cuda._sleep(int(max(1.0, 0.06 * steps) * 1e-3 * 2.4e9))  # ~60 us of host time per call
+    except Exception:
+        pass
     e0.record(stream)
     for i in range(steps):
         fn(i)
@@ -256,7 +246,7 @@ def _time_calls(torch, fn, steps, warmup):
     return e0.elapsed_time(e1) * 1e3 / steps
 
 
-def time_extensions(torch, va, W, steps, replicas):
+def time_extensions(torch, va, W, steps, warmup, replicas):
     """The paths around verify: tree-masked verify and page-table verify on
     the headline shape (cold, rotating replicas), the draft K/V append and the
     kv_indices build.  Returns a dict of µs and GB/s."""
@@ -290,7 +280,7 @@ def time_extensions(torch, va, W, steps, replicas):
     us = _time_calls(torch, lambda i: va.verify_attn_run_tree(
         *(lambda p: (p.q, p.k_ext, p.v_ext, p.k_buf, p.v_buf, p.qo_indptr, p.kv_indptr, p.kv_indices,
                      p.l_ext, mask, mi, p.sm_scale, p.k_scale, p.v_scale))(probs[i % replicas]),
-        out=out, workspace=ws, desc=desc), steps, 5)
+        out=out, workspace=ws, desc=desc), steps, warmup)
     res["tree_verify_b8_8k"] = {"us_per_call": round(us, 3), "gbs": round(kvb / us / 1e3, 2)}
 
     # page-table verify, 16-token pages over the same pool rows count
@@ -302,7 +292,7 @@ def time_extensions(torch, va, W, steps, replicas):
         *(lambda p, t: (p.q, p.k_ext, p.v_ext, p.k_buf, p.v_buf, p.qo_indptr, p.kv_indptr, t, P, p.l_ext,
                         sum(p.prefix_lens), p.sm_scale, p.k_scale, p.v_scale))(probs[i % replicas],
                                                                               tables[i % replicas]),
-        out=out, workspace=ws, desc=desc), steps, 5)
+        out=out, workspace=ws, desc=desc), steps, warmup)
     res["paged16_verify_b8_8k"] = {"us_per_call": round(us, 3), "gbs": round(kvb / us / 1e3, 2)}
     del probs, tables
     torch.cuda.empty_cache()
@@ -317,7 +307,7 @@ def time_extensions(torch, va, W, steps, replicas):
         loc = torch.randperm(pool, device=dev)[:ntok]
         kb = torch.zeros(pool, 2, 256, device=dev).to(kv_dtype)
         vb = torch.zeros(pool, 2, 256, device=dev).to(kv_dtype)
-        us = _time_calls(torch, lambda i: va.verify_attn_append_kv(k, v, loc, kb, vb, 0.05, 0.05), steps, 5)
+        us = _time_calls(torch, lambda i: va.verify_attn_append_kv(k, v, loc, kb, vb, 0.05, 0.05), steps, warmup)
         eb = 1 if kv_dtype == torch.float8_e4m3fn else 2
         moved = ntok * 2 * 512 * (2 + eb) + ntok * 8
         res[tag] = {"us_per_call": round(us, 3), "gbs": round(moved / us / 1e3, 2), "bytes": moved}
@@ -330,7 +320,7 @@ def time_extensions(torch, va, W, steps, replicas):
     sl = torch.full((bs,), n, dtype=torch.int32, device=dev)
     kvp = torch.empty(bs + 1, dtype=torch.int32, device=dev)
     kvi = torch.empty(bs * n, dtype=torch.int64, device=dev)
-    us = _time_calls(torch, lambda i: va.verify_attn_build_kv_indices(rt, rp, sl, kvp, kvi), steps, 5)
+    us = _time_calls(torch, lambda i: va.verify_attn_build_kv_indices(rt, rp, sl, kvp, kvi), steps, warmup)
     moved = bs * n * (4 + 8)
     res["build_kv_indices_b8_8k"] = {"us_per_call": round(us, 3), "gbs": round(moved / us / 1e3, 2),
                                      "bytes": moved}
@@ -416,7 +406,8 @@ def main():
     secondary = {}
     if not args.quick:
         for name, reps in (("b4_64k", 1), ("fp8_ragged", 8), ("decode_b64", 2), ("draft_extend_b16", 8)):
-            r = time_workload(torch, va, W, name, max(20, args.steps // 4), 5, reps, seed0=2000)
+            r = time_workload(torch, va, W, name, max(20, args.steps // 4), max(5, args.warmup // 4), reps,
+                              seed0=2000)
             secondary[name] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in r.items()
                                if k not in ("problem", "name")}
             print("[bench] %s: %.2f us/step (%.1f GB/s), prefix %.2f us back to back (%.1f GB/s)"
@@ -427,7 +418,7 @@ def main():
 
     extensions = {}
     if not args.quick:
-        extensions = time_extensions(torch, va, W, max(20, args.steps // 4), args.replicas)
+        extensions = time_extensions(torch, va, W, max(20, args.steps // 4), args.warmup, args.replicas)
         print("[bench] around verify: %s" % json.dumps(extensions), file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
 
@@ -438,7 +429,7 @@ def main():
 
     p = head["problem"]
     traffic = recorded_traffic()
-    achieved = head["prefix_gbs"]
+    achieved = head["prefix_gbs_b2b"]
     line = {
         "metric": "verify-attn achieved HBM GB/s and us/call (B=8, 8k prefix, l_ext=4, D=256)",
         "value": round(head["gbs"], 2),
@@ -469,9 +460,10 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
             "kernel": "prefix_kernel<bf16, D=256, one 32-row query block>",
-            "kernel_us": head["prefix_us_mean"],
-            "kernel_timing": "mean of HIP events around each of %d prefix launches (cold, rotating "
-                             "replicas) on the launch stream" % args.steps,
+            "kernel_us": head["prefix_us_b2b"],
+            "kernel_timing": "HIP events on the launch stream around %d back-to-back prefix launches "
+                             "(cold, rotating replicas) after %d warm-up launches, per launch"
+                             % (args.steps, args.warmup),
             "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
         },
         "cpu_baseline": cpu,
