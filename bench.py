@@ -29,7 +29,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "speculative_decoding_attention_amd", "csrc", "va_kernels.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefix_kernel_b8_8k_traffic.txt")
+PROFILES = os.path.join(ROOT, "profiles")
 
 
 def parse_args():
@@ -57,12 +57,13 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
-def recorded_traffic():
-    """HBM bytes per prefix launch from the committed counter summary, or None
-    if it is missing or was taken on a different kernel source."""
+def recorded_traffic(workload):
+    """HBM bytes per prefix launch from the committed counter summary of this
+    workload, or None if it is missing or was taken on a different kernel
+    source."""
     try:
         fields = {}
-        with open(TRAFFIC_FILE) as f:
+        with open(os.path.join(PROFILES, "prefix_kernel_%s_traffic.txt" % workload)) as f:
             for line in f:
                 if ":" in line and not line.startswith("#"):
                     k, v = line.split(":", 1)
@@ -139,7 +140,8 @@ def time_workload(torch, va, W, name, steps, warmup, replicas, seed0=1000):
     runners = [Runner(va, p, ws, out) for p in probs]
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
-    kv_bytes = p0.kv_bytes()
+    # the timed loops rotate over the replicas: their mean size (ragged replicas differ)
+    kv_bytes = sum(p.kv_bytes() for p in probs) / len(probs)
 
     def step(i):
         r = runners[i % replicas]
@@ -428,7 +430,18 @@ def main():
         print("[bench] cpu oracle: %s" % json.dumps(cpu), file=sys.stderr, flush=True)
 
     p = head["problem"]
-    traffic = recorded_traffic()
+    traffic = recorded_traffic(args.workload)
+    lens = sorted(set(p.prefix_lens))
+    prefix_desc = ("prefix %d each" % lens[0]) if len(lens) == 1 else (
+        "prefix lengths %d..%d (seeded)" % (lens[0], lens[-1]))
+    pool_desc = "%s pool (%s kv_indices)" % ("fp8 e4m3" if p.kv_fp8 else "bf16",
+                                               "scattered" if p.k_buf.shape[0] > p.total_prefix else "contiguous")
+    workload_desc = "%s: B=%d, %s, l_ext=%d, h_q=%d, h_kv=%d, D=Dv=%d, %s, k_scale=%g, v_scale=%g" % (
+        args.workload, p.bs, prefix_desc, p.l_ext, p.h_q, p.h_kv, p.head_dim, pool_desc, p.k_scale, p.v_scale)
+    qblocks = 1 if head["plan"]["rows"] <= 32 else 2
+    kernel_desc = "prefix_kernel<%s, D=%d, %s>" % ("fp8" if p.kv_fp8 else "bf16", p.head_dim,
+                                                    "one 32-row query block" if qblocks == 1 else
+                                                    "two 32-row query blocks")
     achieved = head["prefix_gbs_b2b"]
     line = {
         "metric": "verify-attn achieved HBM GB/s and us/call (B=8, 8k prefix, l_ext=4, D=256)",
@@ -445,8 +458,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": "b8_8k: B=8, prefix 8192 each, l_ext=4, h_q=16, h_kv=2, D=Dv=256, bf16 pool "
-                        "(2x needed rows, scattered kv_indices), k_scale=0.5, v_scale=0.25",
+            "workload": workload_desc,
             "batch": p.bs, "prefix": p.prefix_lens[0], "l_ext": p.l_ext, "h_q": p.h_q,
             "h_kv": p.h_kv, "head_dim": p.head_dim, "kv_bytes": head["kv_bytes"],
             "cache": "cold (rotating %d replicas)" % args.replicas,
@@ -459,7 +471,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": "prefix_kernel<bf16, D=256, one 32-row query block>",
+            "kernel": kernel_desc,
             "kernel_us": head["prefix_us_b2b"],
             "kernel_timing": "HIP events on the launch stream around %d back-to-back prefix launches "
                              "(cold, rotating replicas) after %d warm-up launches, per launch"
