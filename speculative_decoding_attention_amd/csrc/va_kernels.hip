@@ -749,8 +749,11 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64, 2) void prefix_kernel(
         const uint8_t *V = K + G::STAGE_K;
 
         // one 32-token sub-tile; tokens past the range are masked only in the
-        // (at most one) sub-tile that straddles the end
-        auto sub_tile = [&](const int sub, auto masked) {
+        // (at most one) sub-tile that straddles the end.  One body serves both
+        // cases (the mask is a branch inside it): two instances of the body
+        // made the compiler copy the output accumulators in and out of every
+        // tile to reconcile their register assignments.
+        auto sub_tile = [&](const int sub, const bool masked) {
             const int tok0 = t * TN + sub * 32;  // first token of the sub-tile
 
             // ---- scores S^T[token][query row] of this wave's block, 32 x 32 ----
@@ -783,7 +786,7 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64, 2) void prefix_kernel(
             sc += sc2;
 
             // ---- softmax: lane holds 16 of the row's 32 tokens, lane^32 the rest ----
-            if constexpr (decltype(masked)::value) {
+            if (masked) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int tok = tok0 + 8 * (v >> 2) + 4 * half + (v & 3);
@@ -873,10 +876,7 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64, 2) void prefix_kernel(
             const int tok0 = t * TN + sub * 32;
             if (tok0 >= len)
                 break;  // rest of the last tile is past the range
-            if (tok0 + 32 > len)
-                sub_tile(sub, std::true_type{});
-            else
-                sub_tile(sub, std::false_type{});
+            sub_tile(sub, tok0 + 32 > len);
         }
     }
     wait_vm<0>();  // trailing index copies
