@@ -749,11 +749,14 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64, 2) void prefix_kernel(
         const uint8_t *V = K + G::STAGE_K;
 
         // one 32-token sub-tile; tokens past the range are masked only in the
-        // (at most one) sub-tile that straddles the end.  One body serves both
-        // cases (the mask is a branch inside it): two instances of the body
-        // made the compiler copy the output accumulators in and out of every
-        // tile to reconcile their register assignments.
-        auto sub_tile = [&](const int sub, const bool masked) {
+        // (at most one) sub-tile that straddles the end.  `masked` is a bool
+        // (fp8 pools: one body with the mask as a branch inside it) or a
+        // std::bool_constant (bf16 pools: a masked and an unmasked body).  Two
+        // bodies make the compiler copy the output accumulators in and out of
+        // every tile to reconcile their register assignments (64 moves a tile
+        // on fp8 D=128), which the issue-bound fp8 loop pays for; the
+        // memory-bound bf16 loop measured faster with two bodies all the same.
+        auto sub_tile = [&](const int sub, auto masked) {
             const int tok0 = t * TN + sub * 32;  // first token of the sub-tile
 
             // ---- scores S^T[token][query row] of this wave's block, 32 x 32 ----
@@ -786,7 +789,12 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64, 2) void prefix_kernel(
             sc += sc2;
 
             // ---- softmax: lane holds 16 of the row's 32 tokens, lane^32 the rest ----
-            if (masked) {
+            bool mask_now;
+            if constexpr (std::is_same<decltype(masked), bool>::value)
+                mask_now = masked;
+            else
+                mask_now = decltype(masked)::value;
+            if (mask_now) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int tok = tok0 + 8 * (v >> 2) + 4 * half + (v & 3);
@@ -876,7 +884,12 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64, 2) void prefix_kernel(
             const int tok0 = t * TN + sub * 32;
             if (tok0 >= len)
                 break;  // rest of the last tile is past the range
-            sub_tile(sub, tok0 + 32 > len);
+            if constexpr (FP8)
+                sub_tile(sub, tok0 + 32 > len);
+            else if (tok0 + 32 > len)
+                sub_tile(sub, std::true_type{});
+            else
+                sub_tile(sub, std::false_type{});
         }
     }
     wait_vm<0>();  // trailing index copies
