@@ -540,11 +540,17 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64, 2) void prefix_kernel(
                   __builtin_amdgcn_readfirstlane(st + G::STAGE_K + i * 1024));
         }
     };
-    // query tile -> ring stage NBUF-1 (bf16 rows of D, row-major)
+    // query tile -> ring stage NBUF-1: bf16 rows of D, chunk c of local row r
+    // at chunk c ^ qswz(r).  Each lane later reads its own row, so without the
+    // swizzle the 32 rows (a multiple of 256 bytes apart for D >= 128) would
+    // all hit the same LDS banks.
     constexpr int QCH = D / 8;                    // 16-byte chunks per query row
     constexpr int QI = NQB * 32 * QCH / 64;       // wave-wide copies for the tile
     constexpr int QPW = QI / NW;                  // of which each wave issues
     static_assert(QI % NW == 0, "query copies split evenly over the waves");
+    constexpr int QSW_SHIFT = D * 2 >= 256 ? 0 : (D * 2 == 128 ? 1 : 2);  // rows sharing 256 bytes
+    constexpr int QSW_MASK = (QCH < 16 ? QCH : 16) - 1;
+    auto qswz = [](int r) { return (r >> QSW_SHIFT) & QSW_MASK; };
     auto issue_query = [&]() {
         const int rows = p.rows;
 #pragma unroll
@@ -554,8 +560,9 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64, 2) void prefix_kernel(
             const int r = row0 + e / QCH;             // query row of this chunk
             const int rr = r < rows ? r : row0;       // padding rows copy a valid row
             const int hg = rr / p.l_ext, di = rr % p.l_ext;
+            const int ch = (e % QCH) ^ qswz(e / QCH);  // source chunk of this LDS chunk
             const uint16_t *src = p.q + (int64_t)(qo + di) * p.q_s0 +
-                                  (int64_t)(kvh * p.group + hg) * p.q_s1 + (e % QCH) * 8;
+                                  (int64_t)(kvh * p.group + hg) * p.q_s1 + ch * 8;
             dma16(src, __builtin_amdgcn_readfirstlane(ring + (NBUF - 1) * G::STAGE + i * 1024));
         }
     };
@@ -677,18 +684,18 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64, 2) void prefix_kernel(
     typedef typename std::conditional<FP8, i32x8_t, bf16x8_t>::type qop_t;
     qop_t qreg[NQR];
     {
+        // every local row holds a valid query row (padding rows a copy of the
+        // chunk's first row), and a padding row's outputs are never stored
         const int rl = qbw * 32 + l32;
-        const bool rv = row0 + rl < rows;
-        const uint8_t *qrow = s_ring + (NBUF - 1) * G::STAGE + (rv ? rl : 0) * D * 2;
+        const uint8_t *qrow = s_ring + (NBUF - 1) * G::STAGE + rl * D * 2;
+        const int qz = qswz(rl);
         if constexpr (FP8) {
 #pragma unroll
             for (int j = 0; j < NQR; ++j) {
                 i32x8_t codes;
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {  // 16-byte chunk of 8 bf16 values
-                    u32x4_t raw = *(const u32x4_t *)(qrow + (8 * j + 4 * half + c) * 16);
-                    if (!rv)
-                        raw = u32x4_t{0u, 0u, 0u, 0u};
+                    const u32x4_t raw = *(const u32x4_t *)(qrow + ((8 * j + 4 * half + c) ^ qz) * 16);
 #pragma unroll
                     for (int w = 0; w < 2; ++w) {  // 4 codes per dword
                         const float x0 = clamp_e4m3_range(bf16_to_f32(raw[2 * w] & 0xffffu));
@@ -704,10 +711,7 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64, 2) void prefix_kernel(
         } else {
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
-                u32x4_t raw = *(const u32x4_t *)(qrow + (ks * 2 + half) * 16);
-                if (!rv)
-                    raw = u32x4_t{0u, 0u, 0u, 0u};
-                qreg[ks] = as_bf16x8(raw);
+                qreg[ks] = as_bf16x8(*(const u32x4_t *)(qrow + ((ks * 2 + half) ^ qz) * 16));
             }
         }
     }
