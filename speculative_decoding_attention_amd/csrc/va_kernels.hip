@@ -952,18 +952,24 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64, 2) void prefix_kernel(
         for (int db = 0; db < DBW; ++db) {
             if (db % TS != ts)
                 continue;
-            oacc[db] *= a_own;
+            // every source block's reads first, then the sums: with the reads
+            // interleaved, the compiler kept two of them in flight at a time
+            f32x4_t o[TS - 1][4];
 #pragma unroll
             for (int k = 0; k < TS - 1; ++k) {
                 const float *src = ob + (db * (TS - 1) + k) * BLK + l32 * OST + 4 * half;
 #pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) {
-                    const f32x4_t o = *(const f32x4_t *)(src + 8 * g4);
+                for (int g4 = 0; g4 < 4; ++g4)
+                    o[k][g4] = *(const f32x4_t *)(src + 8 * g4);
+            }
+            oacc[db] *= a_own;
+#pragma unroll
+            for (int k = 0; k < TS - 1; ++k)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4)
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        oacc[db][4 * g4 + e] += a_src[k] * o[e];
-                }
-            }
+                        oacc[db][4 * g4 + e] += a_src[k] * o[k][g4][e];
         }
         lrow = lsum;
         m_ref = mx;
