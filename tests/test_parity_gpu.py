@@ -137,6 +137,16 @@ def test_extend_lengths(va, l_ext):
     check_full(va, W.make_problem([1024, 1024], l_ext, 16, 2, 256, seed=54, name="l_ext %d" % l_ext))
 
 
+@pytest.mark.parametrize("l_ext", [63, 64, 65, 100])
+@pytest.mark.parametrize("kv_dtype", [torch.bfloat16, torch.float8_e4m3fn])
+def test_long_draft_blocks(va, l_ext, kv_dtype):
+    # the combine pass keeps the visible draft keys of a row as a 64-bit word:
+    # rows 63 and 64 sit on its edge, rows past 64 take only the online loop;
+    # 2 * l_ext query rows per KV head (up to 200: four row chunks, the last ragged)
+    check_full(va, W.make_problem([300, 517], l_ext, 4, 2, 128, kv_dtype=kv_dtype, seed=55,
+                                  name="l_ext %d %s" % (l_ext, kv_dtype)))
+
+
 @pytest.mark.parametrize("kw", [dict(), dict(n_splits=4), dict(split_tokens=128)])
 def test_many_sequences(va, kw):
     # more than 64 sequences: range lookups walk the index pointers in
