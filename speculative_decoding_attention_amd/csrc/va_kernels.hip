@@ -908,15 +908,17 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64, 2) void prefix_kernel(
     // has max -inf and weight exactly 0; share 0 always saw the range's first
     // token, so the merged max is finite.
     if constexpr (TS > 1) {
-        // (max, sum) per share: [NQB][CS][TS][2][32]; blocks: [NQB][CS][DBW]
-        // [TS - 1 sources][32 rows][OST], rows padded to 36 floats so that the
-        // 16-byte accesses of 16 lanes fall on distinct banks
-        constexpr int OST = 36;
+        // (max, sum) per share: [NQB][CS][TS][2][32] floats; blocks: [NQB][CS]
+        // [DBW][TS - 1 sources][32 rows][OST] words of bf16 pairs (the shares
+        // travel rounded to bf16, as the partial outputs leave the kernel; the
+        // owner's own share stays fp32), rows padded to 18 words so that the
+        // 8-byte accesses of 16 lanes fall on distinct banks
+        constexpr int OST = 18;
         constexpr int BLK = 32 * OST;
         constexpr int ML = NQB * CS * TS * 64;
         static_assert((ML + NQB * CS * DBW * (TS - 1) * BLK) * 4 <= NBUF * G::STAGE, "merge slots fit the ring");
         float *ml = (float *)s_ring + (qbw * CS + cs) * TS * 64;
-        float *ob = (float *)s_ring + ML + (qbw * CS + cs) * DBW * (TS - 1) * BLK;
+        uint32_t *ob = (uint32_t *)s_ring + ML + (qbw * CS + cs) * DBW * (TS - 1) * BLK;
         lds_barrier();
         if (half == 0) {
             ml[ts * 64 + l32] = m_ref;
@@ -926,11 +928,11 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64, 2) void prefix_kernel(
         for (int db = 0; db < DBW; ++db) {
             const int owner = db % TS;
             if (owner != ts) {  // source slot of this share in the owner's list
-                float *dst = ob + (db * (TS - 1) + (ts < owner ? ts : ts - 1)) * BLK + l32 * OST + 4 * half;
+                uint32_t *dst = ob + (db * (TS - 1) + (ts < owner ? ts : ts - 1)) * BLK + l32 * OST + 2 * half;
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4)
-                    *(f32x4_t *)(dst + 8 * g4) =
-                        f32x4_t{oacc[db][4 * g4], oacc[db][4 * g4 + 1], oacc[db][4 * g4 + 2], oacc[db][4 * g4 + 3]};
+                    *(u32x2_t *)(dst + 4 * g4) = u32x2_t{pack_bf16x2(oacc[db][4 * g4], oacc[db][4 * g4 + 1]),
+                                                         pack_bf16x2(oacc[db][4 * g4 + 2], oacc[db][4 * g4 + 3])};
             }
         }
         lds_barrier();
@@ -954,13 +956,13 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64, 2) void prefix_kernel(
                 continue;
             // every source block's reads first, then the sums: with the reads
             // interleaved, the compiler kept two of them in flight at a time
-            f32x4_t o[TS - 1][4];
+            u32x2_t o[TS - 1][4];
 #pragma unroll
             for (int k = 0; k < TS - 1; ++k) {
-                const float *src = ob + (db * (TS - 1) + k) * BLK + l32 * OST + 4 * half;
+                const uint32_t *src = ob + (db * (TS - 1) + k) * BLK + l32 * OST + 2 * half;
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4)
-                    o[k][g4] = *(const f32x4_t *)(src + 8 * g4);
+                    o[k][g4] = *(const u32x2_t *)(src + 4 * g4);
             }
             oacc[db] *= a_own;
 #pragma unroll
@@ -968,8 +970,10 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64, 2) void prefix_kernel(
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        oacc[db][4 * g4 + e] += a_src[k] * o[k][g4][e];
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t w = o[k][g4][e >> 1];
+                        oacc[db][4 * g4 + e] += a_src[k] * __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+                    }
         }
         lrow = lsum;
         m_ref = mx;
@@ -1030,7 +1034,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     int32_t n_splits, int32_t h_kv, int32_t rows, const CombineParams p)
 {  // leading arguments preloaded into SGPRs, as for the prefix kernel
     constexpr int VPL = D / 64;  // elements of D / Dv per lane
-    constexpr int PRE = 32;      // partial outputs per load batch (the first in round 2)
+    constexpr int PRE = 32;      // partial outputs per load batch (the first in the second load round)
     constexpr int PRE_D = 8;     // draft rows loaded in the first round
 
     const int lane = threadIdx.x & 63;
@@ -1047,7 +1051,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     const int h = kvh * p.group + hg;
     const int d0 = lane * VPL;
 
-    // ---- round 1: where this sequence's rows and ranges are ----
+    // ---- first load round: where this sequence's rows and ranges are ----
     const int qo = qo_indptr[b];
     const SeqChunk first = load_seq_chunk(kv_indptr, qo_indptr, bs, 0);
     asm volatile("" ::"s"(p.q), "s"(p.k_ext), "s"(p.v_ext), "s"(p.part_o), "s"(p.part_lse), "s"(p.q_s0),
@@ -1062,7 +1066,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
         mrow = p.mask_indptr[b] + (int64_t)di * (kv_indptr[b + 1] - kv_indptr[b] + L) +
                (kv_indptr[b + 1] - kv_indptr[b]);
 
-    // ---- round 2: log-sum-exps, partial outputs, query row, draft rows ----
+    // ---- second load round: log-sum-exps, partial outputs, query row, draft rows ----
     const int64_t lse_step = (int64_t)p.h_kv * p.rows;  // next range, same head and row
     const float *lse_row = p.part_lse + ((int64_t)base * p.h_kv + kvh) * p.rows + r;
     const uint16_t *o_row = p.part_o + (((int64_t)base * p.h_kv + kvh) * p.rows + r) * D + d0;
