@@ -73,12 +73,15 @@ typedef enum {
  *   k_buf  [pool,   h_kv, head_dim]    kv_dtype strides kbuf_stride[0..1]
  *   v_buf  [pool,   h_kv, v_head_dim]  kv_dtype strides vbuf_stride[0..1]
  *   out    [q_rows, h_q,  v_head_dim]  bf16     strides out_stride[0..1]
- * num_kv_indices is the length of kv_indices (a static shape that sizes the
- * work; every kv_indptr entry must lie in [0, num_kv_indices]).
+ * num_kv_indices is the length of kv_indices: a static shape, which may be
+ * the capacity of a buffer sized for the largest batch (as a captured graph
+ * replays it) rather than the batch's own total; every kv_indptr entry must
+ * lie in [0, num_kv_indices].
  * Splitting (both 0 = the library's heuristic: the grid holds one range per
- * resident prefix workgroup, at least one per sequence, and the kernels pick
- * the range size from kv_indptr -- the smallest multiple of 64, at least the
- * planner's split_tokens, whose ranges fit that grid):
+ * resident prefix workgroup, at least one per sequence and at most
+ * ceil(num_kv_indices / 64), and the kernels pick the range size from
+ * kv_indptr on every launch -- the smallest multiple of 64 tokens whose
+ * ranges fit that grid -- so the split follows the lengths actually passed):
  *   split_tokens > 0 : every prefix is cut into ranges of split_tokens tokens
  *                      (a multiple of 64), one work item each;
  *   n_splits > 0     : the pages' rule -- every prefix is cut into n_splits
@@ -108,9 +111,10 @@ typedef struct {
  * l_ext and the CU count; identical for every call with the same inputs, so a
  * workspace sized once stays valid, as graph capture needs). */
 typedef struct {
-    int32_t mode;            /* 0: ranges of split_tokens tokens (or more, see above); 1: n_splits
-                                equal ranges per sequence */
-    int32_t split_tokens;    /* tokens per range (mode 0; the heuristic's smallest size) */
+    int32_t mode;            /* 0: heuristic (range size fitted on the device); 1: n_splits equal
+                                ranges per sequence; 2: ranges of split_tokens tokens */
+    int32_t split_tokens;    /* mode 2: tokens per range; mode 0: the size num_kv_indices tokens in
+                                equal prefixes would get (where the kernels guess each range starts) */
     int32_t n_splits;        /* ranges per sequence (mode 1) */
     int32_t rows;            /* query rows per KV head: (h_q / h_kv) * l_ext */
     int32_t row_chunks;      /* rows are processed in chunks of at most 64 */
@@ -136,12 +140,22 @@ VA_API int verify_attn_plan(const va_desc_t *desc, int32_t l_ext, int32_t num_cu
                             va_plan_t *plan);
 
 /* Workspace size in bytes for (desc, l_ext) on a device with num_cus CUs
- * (num_cus <= 0: the current device).  Equals plan.workspace_bytes. */
+ * (num_cus <= 0: the current device).  Equals plan.workspace_bytes.  The
+ * workspace holds the partial outputs and log-sum-exps of the prefix ranges,
+ * the role of VerifySplitKV's att_out / att_lse scratch in verify_splitkv.py,
+ * which that class sizes once by max_bs so that its address stays fixed.  In
+ * the same spirit the size never decreases as bs or num_kv_indices grow (all
+ * other fields equal): a workspace sized for the largest call serves every
+ * smaller one. */
 VA_API int verify_attn_workspace_bytes(const va_desc_t *desc, int32_t l_ext, int32_t num_cus,
                                        size_t *bytes);
 
 /* Full verify attention: the prefix pass then the combine pass, both on
- * `stream` (a hipStream_t; NULL = the default stream).
+ * `stream` (a hipStream_t; NULL = the default stream).  The operation of
+ * verify_splitkv_fwd / VerifySplitKV.__call__ in sglang's verify_splitkv.py
+ * (stage 1 _verify_prefix_stage1 over the split prefix, stage 2
+ * _verify_combine_stage2 for the range merge, the causal draft block and the
+ * final merge), with the arguments of its problem statement.
  *   q, k_ext, v_ext   draft queries / keys / values (bf16, layouts above)
  *   k_buf, v_buf      prefix pool (desc->kv_dtype)
  *   qo_indptr [bs+1]  int32; must equal b * l_ext (constant extend length)
@@ -150,7 +164,10 @@ VA_API int verify_attn_workspace_bytes(const va_desc_t *desc, int32_t l_ext, int
  *   sm_scale          softmax scale (1/sqrt(head_dim) is the usual value)
  *   k_scale, v_scale  pool dequant multipliers on prefix scores / prefix values
  *   out               bf16 output, written in full (rounded to nearest even)
- *   workspace         device buffer of at least verify_attn_workspace_bytes()
+ *   workspace         device buffer of at least verify_attn_workspace_bytes(),
+ *                     256-byte aligned; caller-owned, contents not preserved
+ * Ownership: the library keeps no pointer after the call; calls that share a
+ * workspace must not overlap in time (same stream, or synchronised).
  * The qo_indptr / kv_indptr / kv_indices preconditions are not checked on the
  * host (that would need a device read); violating them is undefined. */
 VA_API int verify_attn_run(const void *q, const void *k_ext, const void *v_ext,

@@ -1,7 +1,8 @@
 // va_api.cpp -- C entry points that run the two passes on the caller's stream.
 //
 // The flow is the pages' VerifySplitKV.__call__ (sglang verify_splitkv.py):
-// prefix pass into fp32 partials, then the fused combine / draft / merge pass.
+// prefix pass into partials (bf16 normalised outputs, fp32 log-sum-exps; the
+// pages keep fp32 outputs), then the fused combine / draft / merge pass.
 // Differences: the partial buffer is the caller's workspace (the pages cache
 // one per shape, sized by the largest batch), scales are host floats that are
 // validated instead of silently replaced by 1.0, and failures are status codes

@@ -62,7 +62,7 @@ struct PrefixParams {
     float qk_scale_log2;       // sm_scale * k_scale * log2(e)
     float v_scale;
     int32_t bs, h_kv, group, l_ext, rows, row_chunks;
-    int32_t mode, split_tokens, n_splits;
+    int32_t mode, split_tokens, n_splits;  // plan.mode (0 fitted, 1 n_splits, 2 explicit size)
     int32_t total_tokens;  // num_kv_indices
 };
 
@@ -81,7 +81,7 @@ struct CombineParams {
     float sm_scale;
     int32_t bs, h_kv, group, l_ext, rows;
     int32_t mode, split_tokens, n_splits;
-    int32_t range_cap;  // mode 0: ranges per KV head the prefix grid holds
+    int32_t range_cap;  // modes 0, 2: ranges per KV head the prefix grid holds
 };
 
 // Threads per workgroup of the append and kv_indices kernels (va_aux.hip).

@@ -144,12 +144,20 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t 
 
 // ------------------------------------------------------------ range lookup ---
 // Ranges are numbered sequence by sequence; range r of the batch and KV head
-// h writes partial slot r * h_kv + h.  Mode 0: sequence b is cut into
-// ceil(n_b / c) ranges of c tokens (the last one shorter), c fitted on the
-// device (fitted_range_units) so that the batch never needs more ranges than
-// the grid holds.  Mode 1 (the pages' rule): sequence b owns ranges
-// b * n_splits .. + n_splits - 1 of ceil(ceil(n_b / n_splits) / 32) * 32
-// tokens, empty past the end.
+// h writes partial slot r * h_kv + h.
+//   mode 0 (fitted): sequence b of n_b tokens is cut into ceil(n_b / c)
+//     ranges of c tokens (the last one shorter), c = 64 k with k the smallest
+//     positive integer for which the batch needs at most `cap` ranges, cap
+//     being the ranges per (KV head, row chunk) the grid holds (never fewer
+//     than bs, so k = max ceil(n_b / 64), one range per sequence, always
+//     fits).  k comes from the lengths in kv_indptr on every launch, so the
+//     split follows the batch actually passed whatever the length of
+//     kv_indices: a buffer sized for the largest batch, as a captured graph
+//     replays it with other lengths, splits the same as an exact one.
+//   mode 1 (the pages' rule): sequence b owns ranges b * n_splits ..
+//     + n_splits - 1 of ceil(ceil(n_b / n_splits) / 32) * 32 tokens, empty
+//     past the end.
+//   mode 2 (explicit): as mode 0 with c = split_tokens.
 struct Range {
     int32_t b;
     int32_t start;    // token range [start, end) of sequence b's prefix
@@ -159,18 +167,108 @@ struct Range {
     bool valid;
 };
 
-// Index pointers of 64 consecutive sequences b0 + lane (clamped to the last
-// sequence so that every load is in bounds and unconditional: the compiler
-// then issues all three before the first wait).
-struct SeqChunk {
-    int32_t k0, k1, q0;  // kv_indptr[b], kv_indptr[b + 1], qo_indptr[b]
+// Index pointers of the sequences b0 + 64 c + lane, c < NC, each clamped to
+// the last sequence so that every load is in bounds and unconditional (the
+// compiler then issues all of them before the first wait).  One group holds
+// 64 NC sequences in registers: NC = 1 serves batches of up to 64 sequences,
+// NC = 8 up to 512, from a single load round; larger batches walk further
+// groups, each loaded again where it is needed.
+template <int NC>
+struct SeqGroup {
+    int32_t k0[NC], k1[NC], q0[NC];  // kv_indptr[b], kv_indptr[b + 1], qo_indptr[b]
 };
 
-__device__ __forceinline__ SeqChunk load_seq_chunk(const int32_t *kv_indptr, const int32_t *qo_indptr,
-                                                   int32_t bs, int32_t b0)
+template <int NC>
+__device__ __forceinline__ SeqGroup<NC> load_group(const int32_t *kv_indptr, const int32_t *qo_indptr,
+                                                    int32_t bs, int32_t b0)
 {
-    const int32_t b = min(b0 + (int32_t)(threadIdx.x & 63), bs - 1);
-    return SeqChunk{kv_indptr[b], kv_indptr[b + 1], qo_indptr[b]};
+    SeqGroup<NC> g;
+    const int32_t lane = (int32_t)(threadIdx.x & 63);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const int32_t b = min(b0 + 64 * c + lane, bs - 1);
+        g.k0[c] = kv_indptr[b];
+        g.k1[c] = kv_indptr[b + 1];
+        g.q0[c] = qo_indptr[b];
+    }
+    return g;
+}
+
+// prefix length of sequence b0 + 64 c + lane (0 past the batch)
+template <int NC>
+__device__ __forceinline__ uint32_t seq_len(const SeqGroup<NC> &g, int c, int32_t b0, int32_t bs)
+{
+    return b0 + 64 * c + (int32_t)(threadIdx.x & 63) < bs ? (uint32_t)(g.k1[c] - g.k0[c]) : 0u;
+}
+
+// ranges of 64 k tokens that cover a prefix of n tokens
+__device__ __forceinline__ uint32_t ranges_for(uint32_t n, uint32_t k)
+{
+    return (((n + 63u) >> 6) + k - 1u) / k;
+}
+
+// number of ranges of 64 k tokens the whole batch needs (whole-wave call)
+template <int NC>
+__device__ __forceinline__ uint32_t batch_ranges(const int32_t *kv_indptr, const int32_t *qo_indptr, int32_t bs,
+                                                 uint32_t k, const SeqGroup<NC> &first)
+{
+    uint32_t t = 0;
+    for (int32_t b0 = 0; b0 < bs; b0 += 64 * NC) {
+        const SeqGroup<NC> g = b0 == 0 ? first : load_group<NC>(kv_indptr, qo_indptr, bs, b0);
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+            t += ranges_for(seq_len(g, c, b0, bs), k);
+    }
+    return (uint32_t)wave_sum_i((int32_t)t);
+}
+
+// Mode 0: the range size in units of 64 tokens (whole-wave call).  With
+// m_b = ceil(n_b / 64) and M their sum, count(k) = sum_b ceil(m_b / k) is at
+// least M / k and at most M / k + bs, so the answer lies in
+// [ceil(M / cap), ceil(M / (cap - bs))] (when cap > bs) and never above
+// max m_b; a binary search over whole-batch counts takes it from there.
+template <int NC>
+__device__ __forceinline__ uint32_t fitted_range_units(const int32_t *kv_indptr, const int32_t *qo_indptr,
+                                                       int32_t bs, int32_t cap, const SeqGroup<NC> &first)
+{
+    uint32_t ms = 0, mx = 0;
+    for (int32_t b0 = 0; b0 < bs; b0 += 64 * NC) {
+        const SeqGroup<NC> g = b0 == 0 ? first : load_group<NC>(kv_indptr, qo_indptr, bs, b0);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const uint32_t m = (seq_len(g, c, b0, bs) + 63u) >> 6;
+            ms += m;
+            mx = max(mx, m);
+        }
+    }
+    const uint32_t msum = (uint32_t)wave_sum_i((int32_t)ms);
+    const uint32_t mmax = (uint32_t)wave_max_i((int32_t)mx);
+    const uint32_t ucap = (uint32_t)cap;
+    if (msum == 0)
+        return 1u;  // no prefix token: any size
+    uint32_t lo = max((msum + ucap - 1u) / ucap, 1u);
+    if (batch_ranges(kv_indptr, qo_indptr, bs, lo, first) <= ucap)
+        return lo;  // every uniform batch whose lengths are multiples of the size
+    uint32_t hi = mmax;
+    if (ucap > (uint32_t)bs)
+        hi = min(hi, (msum + (ucap - (uint32_t)bs) - 1u) / (ucap - (uint32_t)bs));
+    while (lo + 1u < hi) {  // count(lo) > cap >= count(hi)
+        const uint32_t mid = lo + (hi - lo) / 2u;
+        if (batch_ranges(kv_indptr, qo_indptr, bs, mid, first) <= ucap)
+            hi = mid;
+        else
+            lo = mid;
+    }
+    return hi;
+}
+
+// Range size of modes 0 and 2 in units of 64 tokens.
+template <int NC>
+__device__ __forceinline__ uint32_t range_units(const int32_t *kv_indptr, const int32_t *qo_indptr, int32_t bs,
+                                                int32_t mode, int32_t split_tokens, int32_t cap,
+                                                const SeqGroup<NC> &first)
+{
+    return mode == 2 ? (uint32_t)split_tokens >> 6 : fitted_range_units<NC>(kv_indptr, qo_indptr, bs, cap, first);
 }
 
 // Mode 1: range `cidx` -> its sequence, token range and index pointers.
@@ -195,58 +293,6 @@ __device__ __forceinline__ Range locate_range(const int32_t *kv_indptr, const in
     return r;
 }
 
-// Mode 0 range size.  Sequence b of n_b tokens gets ceil(n_b / c) ranges of c
-// tokens; c = 64 k with k the smallest integer >= split_tokens / 64 for which
-// the batch needs at most `cap` ranges (the grid's ranges per KV head and row
-// chunk; the planner makes cap >= bs, so k = max ceil(n_b / 64) always fits).
-// With m_b = ceil(n_b / 64), sequence b's range count is ceil(m_b / k).
-// Whole-wave; `first` holds sequences 0..63.
-__device__ __forceinline__ int32_t ranges_in_chunk(const SeqChunk &c, int32_t b0, int32_t bs, uint32_t k)
-{
-    const int lane = threadIdx.x & 63;
-    const uint32_t n = b0 + lane < bs ? (uint32_t)(c.k1 - c.k0) : 0u;
-    const uint32_t m = (n + 63u) >> 6;
-    return wave_sum_i((int32_t)((m + k - 1u) / k));
-}
-
-__device__ __forceinline__ int32_t fitted_range_units(const int32_t *kv_indptr, const int32_t *qo_indptr,
-                                                      int32_t bs, int32_t split_tokens, int32_t cap,
-                                                      const SeqChunk &first)
-{
-    auto count = [&](uint32_t k) {
-        int32_t t = ranges_in_chunk(first, 0, bs, k);
-        for (int32_t b0 = 64; b0 < bs; b0 += 64)
-            t += ranges_in_chunk(load_seq_chunk(kv_indptr, qo_indptr, bs, b0), b0, bs, k);
-        return t;
-    };
-    uint32_t lo = (uint32_t)split_tokens >> 6;
-    if (count(lo) <= cap)
-        return (int32_t)lo;  // every uniform batch the planner sized
-    // count(k) <= M / k + bs with M = sum m_b, so k = ceil(M / (cap - bs))
-    // fits when cap > bs; k = max m_b fits always (one range per sequence)
-    const int lane = threadIdx.x & 63;
-    int32_t msum = 0, mmax = 0;
-    for (int32_t b0 = 0; b0 < bs; b0 += 64) {
-        const SeqChunk c = b0 == 0 ? first : load_seq_chunk(kv_indptr, qo_indptr, bs, b0);
-        const int32_t n = b0 + lane < bs ? c.k1 - c.k0 : 0;
-        const int32_t m = (n + 63) >> 6;
-        msum += wave_sum_i(m);
-        mmax = max(mmax, wave_max_i(m));
-    }
-    uint32_t hi = (uint32_t)mmax;
-    if (cap > bs)
-        hi = min(hi, (uint32_t)((msum + (cap - bs) - 1) / (cap - bs)));
-    hi = max(hi, lo + 1);
-    while (lo + 1 < hi) {  // count(lo) > cap >= count(hi)
-        const uint32_t mid = lo + (hi - lo) / 2;
-        if (count(mid) <= cap)
-            hi = mid;
-        else
-            lo = mid;
-    }
-    return (int32_t)hi;
-}
-
 // inclusive prefix sum over the lanes
 __device__ __forceinline__ int wave_scan_incl(int x)
 {
@@ -259,63 +305,68 @@ __device__ __forceinline__ int wave_scan_incl(int x)
     return x + (lane >= 16 ? t0 : 0) + (lane >= 32 ? t1 : 0) + (lane >= 48 ? t2 : 0);
 }
 
-// Mode 0: range `cidx` -> its sequence, token range and index pointers
-// (ranges numbered sequence by sequence).
-__device__ __forceinline__ Range locate_fitted_range(const int32_t *kv_indptr, const int32_t *qo_indptr,
-                                                     int32_t bs, int32_t split_tokens, int32_t cap,
-                                                     int64_t cidx, const SeqChunk &first)
+// Modes 0 and 2: range `cidx` -> its sequence, token range and index
+// pointers, for ranges of 64 k tokens numbered sequence by sequence.
+template <int NC>
+__device__ __forceinline__ Range locate_split_range(const int32_t *kv_indptr, const int32_t *qo_indptr,
+                                                    int32_t bs, uint32_t k, int64_t cidx,
+                                                    const SeqGroup<NC> &first)
 {
     Range r = {0, 0, 0, 0, 0, false};
-    const uint32_t k = (uint32_t)fitted_range_units(kv_indptr, qo_indptr, bs, split_tokens, cap, first);
-    const int32_t c = (int32_t)(k << 6);
-    const int lane = threadIdx.x & 63;
+    const int32_t c_tok = (int32_t)(k << 6);
     int64_t cum = 0;
-    for (int32_t b0 = 0; b0 < bs; b0 += 64) {
-        const SeqChunk ch = b0 == 0 ? first : load_seq_chunk(kv_indptr, qo_indptr, bs, b0);
-        const int32_t n = b0 + lane < bs ? ch.k1 - ch.k0 : 0;
-        const int32_t nch = (int32_t)((((uint32_t)n + 63u) >> 6) + k - 1u) / (int32_t)k;
-        const int32_t incl = wave_scan_incl(nch);
-        const int32_t total = lane_i(incl, 63);
-        if (cidx < cum + total) {
-            const uint64_t hit = __ballot(cum + incl > cidx);
-            const int h = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)hit) - 1);
-            const int32_t ci = (int32_t)(cidx - cum - lane_i(incl - nch, h));
-            r.b = b0 + h;
-            r.start = ci * c;
-            r.end = min(r.start + c, lane_i(n, h));
-            r.kv_base = lane_i(ch.k0, h);
-            r.qo = lane_i(ch.q0, h);
-            r.valid = true;
-            return r;
+    for (int32_t b0 = 0; b0 < bs; b0 += 64 * NC) {
+        const SeqGroup<NC> g = b0 == 0 ? first : load_group<NC>(kv_indptr, qo_indptr, bs, b0);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const uint32_t n = seq_len(g, c, b0, bs);
+            const int32_t nch = (int32_t)ranges_for(n, k);
+            const int32_t incl = wave_scan_incl(nch);
+            const int32_t total = lane_i(incl, 63);
+            if (cidx < cum + total) {
+                const uint64_t hit = __ballot(cum + incl > cidx);
+                const int h = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)hit) - 1);
+                const int32_t ci = (int32_t)(cidx - cum - lane_i(incl - nch, h));
+                r.b = b0 + 64 * c + h;
+                r.start = ci * c_tok;
+                r.end = min(r.start + c_tok, lane_i((int32_t)n, h));
+                r.kv_base = lane_i(g.k0[c], h);
+                r.qo = lane_i(g.q0[c], h);
+                r.valid = true;
+                return r;
+            }
+            cum += total;
         }
-        cum += total;
     }
     return r;
 }
 
 // First partial slot and slot count of sequence b (whole-wave call).
+template <int NC>
 __device__ __forceinline__ void ranges_of(const int32_t *kv_indptr, const int32_t *qo_indptr, int32_t bs,
                                           int32_t mode, int32_t split_tokens, int32_t n_splits, int32_t cap,
-                                          int32_t b, const SeqChunk &first, int32_t *base, int32_t *count)
+                                          int32_t b, const SeqGroup<NC> &first, int32_t *base, int32_t *count)
 {
     if (mode == 1) {
         *base = b * n_splits;
         *count = n_splits;
         return;
     }
-    const uint32_t k = (uint32_t)fitted_range_units(kv_indptr, qo_indptr, bs, split_tokens, cap, first);
-    const int lane = threadIdx.x & 63;
-    int32_t acc = 0, own = 0;
-    for (int32_t b0 = 0; b0 <= b; b0 += 64) {
-        const SeqChunk c = b0 == 0 ? first : load_seq_chunk(kv_indptr, qo_indptr, bs, b0);
-        const int32_t bb = b0 + lane;
-        const uint32_t m = ((uint32_t)(bb < bs ? c.k1 - c.k0 : 0) + 63u) >> 6;
-        const int32_t nch = (int32_t)((m + k - 1u) / k);
-        own = bb == b ? nch : own;
-        acc += wave_sum_i(bb < b ? nch : 0);
+    const uint32_t k = range_units<NC>(kv_indptr, qo_indptr, bs, mode, split_tokens, cap, first);
+    const int32_t lane = (int32_t)(threadIdx.x & 63);
+    uint32_t acc = 0, own = 0;
+    for (int32_t b0 = 0; b0 <= b; b0 += 64 * NC) {
+        const SeqGroup<NC> g = b0 == 0 ? first : load_group<NC>(kv_indptr, qo_indptr, bs, b0);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const int32_t bb = b0 + 64 * c + lane;
+            const uint32_t nch = ranges_for(seq_len(g, c, b0, bs), k);
+            own = bb == b ? nch : own;
+            acc += bb < b ? nch : 0u;
+        }
     }
-    *base = acc;
-    *count = lane_i(own, __builtin_amdgcn_readfirstlane(b & 63));
+    *base = wave_sum_i((int32_t)acc);
+    *count = lane_i((int32_t)own, __builtin_amdgcn_readfirstlane(b & 63));
 }
 
 // ----------------------------------------------------------- prefix kernel ---
@@ -568,41 +619,56 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64, 2) void prefix_kernel(
     };
 
     // ---- range ----
-    // Mode 0: every prefix is cut into ranges of c tokens (the last one of a
-    // sequence shorter), c the smallest multiple of 64 that is at least
-    // split_tokens and gives no more ranges than the grid holds.  When every
-    // prefix is a multiple of split_tokens, range cidx starts at kv_indices
-    // position cidx * split_tokens: its first three index copies go out before
-    // the index pointers are read, and are used if the range really starts
-    // there.  Mode 1 (the pages' rule): range cidx is split cidx % n_splits of
+    // Modes 0 and 2 cut every prefix into ranges of c tokens; split_tokens is
+    // c itself (mode 2) or the planner's estimate of it (mode 0: the size that
+    // num_kv_indices tokens in equal prefixes would get).  If every prefix is
+    // a multiple of it, range cidx starts at kv_indices position
+    // cidx * split_tokens: its first three index copies go out before the
+    // index pointers are read, and are used if the range really starts there.
+    // Mode 1 (the pages' rule): range cidx is split cidx % n_splits of
     // sequence cidx / n_splits.
-    const SeqChunk first = load_seq_chunk(kv_indptr, qo_indptr, bs, 0);
     int64_t P0 = -1;
     int early_fetch = 0;
-    if (mode == 0 && !paged) {
-        const int64_t g0 = cidx * (int64_t)split_tokens;
-        if (g0 < total_tokens) {
-            P0 = g0;
-            kv0 = g0;
-            fetch = (int)min((int64_t)split_tokens, (int64_t)total_tokens - g0);
-            early_fetch = fetch;
-            issue_idx(0);
-            issue_idx(1);
-            issue_idx(2);
+    auto early_copies = [&]() {
+        if (mode != 1 && !paged) {
+            const int64_t g0 = cidx * (int64_t)split_tokens;
+            if (g0 < total_tokens) {
+                P0 = g0;
+                kv0 = g0;
+                fetch = (int)min((int64_t)split_tokens, (int64_t)total_tokens - g0);
+                early_fetch = fetch;
+                issue_idx(0);
+                issue_idx(1);
+                issue_idx(2);
+            }
         }
-    }
-    // the remaining kernel arguments while those loads are in flight (the
-    // scheduling barrier keeps the early copies ahead of their wait; row_chunks
-    // stays live so that no register of the argument loads is reused early)
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("" ::"s"(p.q), "s"(p.k_buf), "s"(p.v_buf), "s"(p.kb_s1), "s"(p.vb_s1), "s"(p.kb_s0),
-                 "s"(p.vb_s0), "s"(p.q_s0), "s"(p.q_s1), "s"(p.group), "s"(p.l_ext), "s"(p.rows),
-                 "s"(p.row_chunks)
-                 : "memory");
-    const int rows = p.rows;
+        // the remaining kernel arguments while those loads are in flight (the
+        // scheduling barrier keeps the early copies ahead of their wait;
+        // row_chunks stays live so that no register of the argument loads is
+        // reused early)
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("" ::"s"(p.q), "s"(p.k_buf), "s"(p.v_buf), "s"(p.kb_s1), "s"(p.vb_s1), "s"(p.kb_s0),
+                     "s"(p.vb_s0), "s"(p.q_s0), "s"(p.q_s1), "s"(p.group), "s"(p.l_ext), "s"(p.rows),
+                     "s"(p.row_chunks)
+                     : "memory");
+    };
     const int32_t range_cap = (int32_t)(gridDim.x / (uint32_t)(h_kv * row_chunks));  // ranges per (KV head, chunk)
-    const Range rg = mode == 0 ? locate_fitted_range(kv_indptr, qo_indptr, bs, split_tokens, range_cap, cidx, first)
-                               : locate_range(kv_indptr, qo_indptr, bs, n_splits, cidx);
+    Range rg;
+    if (mode == 1) {
+        early_copies();
+        rg = locate_range(kv_indptr, qo_indptr, bs, n_splits, cidx);
+    } else if (bs <= 64) {
+        const SeqGroup<1> first = load_group<1>(kv_indptr, qo_indptr, bs, 0);
+        early_copies();
+        const uint32_t k = range_units<1>(kv_indptr, qo_indptr, bs, mode, split_tokens, range_cap, first);
+        rg = locate_split_range<1>(kv_indptr, qo_indptr, bs, k, cidx, first);
+    } else {
+        const SeqGroup<8> first = load_group<8>(kv_indptr, qo_indptr, bs, 0);
+        early_copies();
+        const uint32_t k = range_units<8>(kv_indptr, qo_indptr, bs, mode, split_tokens, range_cap, first);
+        rg = locate_split_range<8>(kv_indptr, qo_indptr, bs, k, cidx, first);
+    }
+    const int rows = p.rows;
     if (!rg.valid) {
         wait_vm<0>();  // early index copies of a surplus slot of the static grid
         return;        // (never read by the combine pass)
@@ -1053,13 +1119,22 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
 
     // ---- first load round: where this sequence's rows and ranges are ----
     const int qo = qo_indptr[b];
-    const SeqChunk first = load_seq_chunk(kv_indptr, qo_indptr, bs, 0);
-    asm volatile("" ::"s"(p.q), "s"(p.k_ext), "s"(p.v_ext), "s"(p.part_o), "s"(p.part_lse), "s"(p.q_s0),
-                 "s"(p.q_s1), "s"(p.ke_s0), "s"(p.ke_s1), "s"(p.ve_s0), "s"(p.ve_s1), "s"(p.group), "s"(p.l_ext),
-                 "s"(p.range_cap)
-                 : "memory");
+    auto pin_args = [&]() {
+        asm volatile("" ::"s"(p.q), "s"(p.k_ext), "s"(p.v_ext), "s"(p.part_o), "s"(p.part_lse), "s"(p.q_s0),
+                     "s"(p.q_s1), "s"(p.ke_s0), "s"(p.ke_s1), "s"(p.ve_s0), "s"(p.ve_s1), "s"(p.group),
+                     "s"(p.l_ext), "s"(p.range_cap)
+                     : "memory");
+    };
     int32_t base, count;
-    ranges_of(kv_indptr, qo_indptr, bs, mode, split_tokens, n_splits, p.range_cap, b, first, &base, &count);
+    if (bs <= 64) {
+        const SeqGroup<1> first = load_group<1>(kv_indptr, qo_indptr, bs, 0);
+        pin_args();
+        ranges_of<1>(kv_indptr, qo_indptr, bs, mode, split_tokens, n_splits, p.range_cap, b, first, &base, &count);
+    } else {
+        const SeqGroup<8> first = load_group<8>(kv_indptr, qo_indptr, bs, 0);
+        pin_args();
+        ranges_of<8>(kv_indptr, qo_indptr, bs, mode, split_tokens, n_splits, p.range_cap, b, first, &base, &count);
+    }
     const int L = p.l_ext;
     int64_t mrow = 0;  // this row's tree-mask bytes for the draft keys
     if (p.mask)

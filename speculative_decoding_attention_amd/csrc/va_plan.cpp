@@ -157,31 +157,36 @@ int make_plan(const va_desc_t *d, int32_t l_ext, int32_t num_cus, va_plan_t *pla
         p.mode = 1;
         p.n_splits = d->n_splits;
         ranges = (int64_t)d->bs * d->n_splits;
-        p.range_slots = ranges;
-    } else {
-        p.mode = 0;
-        int64_t c = d->split_tokens;
-        if (c > 0) {
-            // every prefix cut into ranges of exactly c tokens:
-            // sum_b ceil(n_b / c) <= floor((T + bs * (c - 1)) / c)
-            ranges = (T + (int64_t)d->bs * (c - 1)) / c;
-        } else {
-            // As many ranges as the CUs hold resident prefix workgroups,
-            // never fewer than kSplitQuantum tokens each.  The kernels grow
-            // the range size on the device (in steps of kSplitQuantum) until a
-            // ragged batch fits this count, one range per sequence at least.
-            const int64_t units = (int64_t)d->h_kv * p.row_chunks;
-            const int qb = query_blocks_for(rows < kRowChunk ? (int)rows : kRowChunk);
-            const int64_t target = (int64_t)prefix_resident_per_cu(qb) * num_cus;
-            c = (T * units + target - 1) / target;
-            c = align_up(c < kSplitQuantum ? kSplitQuantum : c, kSplitQuantum);
-            if (c > (1 << 30))
-                c = 1 << 30;
-            ranges = T > 0 ? std::max<int64_t>((T + c - 1) / c, d->bs) : 0;
-        }
+    } else if (d->split_tokens > 0) {
+        // every prefix cut into ranges of exactly c tokens:
+        // sum_b ceil(n_b / c) <= floor((T + bs * (c - 1)) / c)
+        p.mode = 2;
+        const int64_t c = d->split_tokens;
         p.split_tokens = (int32_t)c;
-        p.range_slots = ranges;
+        ranges = (T + (int64_t)d->bs * (c - 1)) / c;
+    } else {
+        // One range per resident prefix workgroup, at least one per sequence
+        // and (for short batches) no more than T / 64 rounded up: ranges are
+        // at least kSplitQuantum tokens.  The count does not depend on T
+        // beyond that cap, so a kv_indices buffer sized for the largest batch
+        // (graph capture) keeps the full grid, and the workspace never
+        // shrinks as T or bs grow.  The kernels fit the range size to the
+        // lengths in kv_indptr on every launch.  split_tokens is only the
+        // size T tokens in equal prefixes would get: the kernels' guess for
+        // where each range starts, so that its first index copies can go out
+        // before kv_indptr has been read.
+        p.mode = 0;
+        const int64_t units = (int64_t)d->h_kv * p.row_chunks;
+        const int qb = query_blocks_for(rows < kRowChunk ? (int)rows : kRowChunk);
+        const int64_t target = (int64_t)prefix_resident_per_cu(qb) * num_cus;
+        int64_t c = (T * units + target - 1) / target;
+        c = align_up(c < kSplitQuantum ? kSplitQuantum : c, kSplitQuantum);
+        p.split_tokens = (int32_t)std::min<int64_t>(c, (int64_t)1 << 30);
+        ranges = T > 0 ? std::max<int64_t>(std::min<int64_t>(target / units, (T + kSplitQuantum - 1) / kSplitQuantum),
+                                           d->bs)
+                       : 0;
     }
+    p.range_slots = ranges;
     const int64_t slots = p.range_slots * d->h_kv;
     p.prefix_blocks = ranges * d->h_kv * p.row_chunks;
     // one wavefront per output row

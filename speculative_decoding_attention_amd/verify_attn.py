@@ -338,9 +338,13 @@ class VerifyAttn:
     """Fixed-address runner for one problem shape family.
 
     Holds a workspace sized once for the largest batch (``max_bs``) and the
-    largest ``num_kv_indices`` it will see, so its address never changes and
-    calls can be captured in a HIP graph (the pages' VerifySplitKV caches its
-    scratch per shape for the same reason).
+    largest ``num_kv_indices`` (``max_kv_indices``) it will see, so its address
+    never changes and calls can be captured in a HIP graph (the pages'
+    VerifySplitKV caches its scratch per shape, sized by max_bs, for the same
+    reason).  The library's workspace size never decreases as the batch or
+    the index count grow, so every call with ``bs <= max_bs`` and
+    ``len(kv_indices) <= max_kv_indices`` fits; ``kv_indices`` may be a buffer
+    of fixed capacity whose used part ``kv_indptr`` delimits.
     """
 
     def __init__(self, h_q, h_kv, head_dim, l_ext, kv_dtype, max_bs, max_kv_indices, device,

@@ -110,29 +110,36 @@ def test_plan_headline_shapes():
     assert plan.workspace_bytes >= plan.range_slots * 2 * 32 * (256 * 2 + 4)
 
 
-def _fitted_units(lens, split_tokens, cap):
-    """The kernels' mode-0 range size in units of 64 tokens: the smallest k >=
-    split_tokens / 64 with sum_b ceil(ceil(n_b / 64) / k) <= cap (plain search)."""
+def _fitted_units(lens, cap):
+    """The kernels' mode-0 range size in units of 64 tokens, by plain search:
+    the smallest k >= 1 with sum_b ceil(ceil(n_b / 64) / k) <= cap."""
     m = [-(-n // 64) for n in lens]
-    k = split_tokens // 64
+    k = 1
     while sum(-(-x // k) for x in m) > cap:
         k += 1
     return k
 
 
+def _meta_with_indices(bs, T, **kw):
+    meta = meta_problem(bs=bs, n=1, **kw)
+    meta["kv_indices"] = torch.empty(T, dtype=torch.int64, device="meta")
+    return meta
+
+
 @pytest.mark.parametrize("seed", range(5))
 def test_ragged_batches_fit_the_resident_workgroups(seed):
-    # Mode 0 (heuristic): the grid holds as many ranges per KV head as the CUs
-    # keep resident (at least one per sequence); the kernels grow the range
-    # size until a ragged batch fits, so no workgroup waits for a second round.
+    # Mode 0 (heuristic): the grid holds one range per resident prefix
+    # workgroup (two 4-wave workgroups per CU here), at least one per sequence
+    # and at most ceil(T / 64); the kernels fit the range size to the lengths
+    # so that a ragged batch never needs more ranges than that.
     g = torch.Generator().manual_seed(seed)
     bs = int(torch.randint(1, 40, (1,), generator=g))
     lens = torch.randint(0, 5000, (bs,), generator=g).tolist()
     T = sum(lens)
-    meta = meta_problem(bs=bs, l_ext=2, h_q=8, h_kv=1, d=128, n=1)
-    meta["kv_indices"] = torch.empty(T, dtype=torch.int64, device="meta")
+    meta = _meta_with_indices(bs, T, l_ext=2, h_q=8, h_kv=1, d=128)
     for cus in (8, 80, 256):
         plan = va.verify_attn_plan(va.make_desc(**meta), 2, cus)
+        assert plan.mode == 0
         c = plan.split_tokens
         assert c % 64 == 0 and c >= 64
         cap = plan.prefix_blocks  # one KV head, one row chunk
@@ -140,21 +147,71 @@ def test_ragged_batches_fit_the_resident_workgroups(seed):
         if T == 0:
             assert cap == 0
             continue
-        assert cap == max(-(-T // c), bs)
-        assert cap <= max(2 * cus, bs, -(-T // 64))  # two resident 4-wave workgroups per CU
-        k = _fitted_units(lens, c, cap)
-        assert k * 64 <= max(c, -(-max(lens) // 64) * 64)
+        assert cap == max(min(2 * cus, -(-T // 64)), bs)
+        k = _fitted_units(lens, cap)
         assert sum(-(-n // (64 * k)) for n in lens) <= cap
+        assert k * 64 <= -(-max(lens) // 64) * 64  # never longer than one range per sequence
+
+
+def test_capacity_sized_kv_indices_keep_the_grid():
+    # Under graph capture kv_indices is a buffer sized for the largest batch
+    # (aiter_backend.py, init_cuda_graph_state: cuda_graph_kv_indices).  The
+    # headline batch (8 x 8192, 16/2 heads, D=256) with that buffer at 1x, 2x,
+    # 4x and 8x its needed length keeps every range slot, and the kernels'
+    # fitted size is the 256 tokens the exact buffer gives.
+    base = None
+    for factor in (1, 2, 4, 8):
+        meta = _meta_with_indices(8, factor * 8 * 8192)
+        plan = va.verify_attn_plan(va.make_desc(**meta), 4, 256)
+        if base is None:
+            base = plan
+        assert plan.range_slots == base.range_slots == 256
+        assert plan.prefix_blocks == base.prefix_blocks == 512
+        assert plan.workspace_bytes == base.workspace_bytes
+        assert _fitted_units([8192] * 8, plan.range_slots) == 4
+
+
+@pytest.mark.parametrize("shape", [
+    dict(l_ext=4, h_q=16, h_kv=2, d=256),
+    dict(l_ext=8, h_q=8, h_kv=1, d=128, kv_dtype=torch.float8_e4m3fn),
+    dict(l_ext=8, h_q=16, h_kv=1, d=64),          # two row chunks
+    dict(l_ext=1, h_q=16, h_kv=2, d=256),         # decode
+])
+@pytest.mark.parametrize("split", [dict(), dict(split_tokens=128), dict(n_splits=8)])
+def test_workspace_is_an_upper_bound_for_smaller_calls(shape, split):
+    # A workspace sized once for (max_bs, T_max) must serve every call with
+    # bs <= max_bs and T <= T_max (VerifySplitKV on page 1 sizes its scratch by
+    # max_bs for the same reason): the size never decreases as T or bs grow.
+    max_bs, t_max = 24, 200_000
+    l_ext = shape["l_ext"]
+    ts = sorted(set([0, 1, 63, 64, 65, 127, 129, 1000, 4095, 4097, 13423, 16423, 65536, t_max] +
+                    list(range(0, t_max + 1, 997))))
+    top = va.verify_attn_workspace_bytes(va.make_desc(**_meta_with_indices(max_bs, t_max, **shape), **split),
+                                         l_ext, 256)
+    for bs in (1, 2, 7, 8, 23, 24):
+        prev = -1
+        for T in ts:
+            n = va.verify_attn_workspace_bytes(va.make_desc(**_meta_with_indices(bs, T, **shape), **split),
+                                               l_ext, 256)
+            assert n >= prev, (bs, T, n, prev)
+            assert n <= top, (bs, T, n, top)
+            prev = n
+    for T in (0, 1000, 65536, t_max):
+        prev = -1
+        for bs in range(1, max_bs + 1):
+            n = va.verify_attn_workspace_bytes(va.make_desc(**_meta_with_indices(bs, T, **shape), **split),
+                                               l_ext, 256)
+            assert n >= prev, (bs, T, n, prev)
+            prev = n
 
 
 def test_explicit_split_tokens_are_kept():
-    # split_tokens given: the grid bound covers every batch at exactly that size
+    # split_tokens given (mode 2): the grid bound covers every batch at exactly that size
     lens = [100, 1, 4097, 64, 0, 700]
-    meta = meta_problem(bs=len(lens), l_ext=2, h_q=8, h_kv=1, d=128, n=1)
-    meta["kv_indices"] = torch.empty(sum(lens), dtype=torch.int64, device="meta")
+    meta = _meta_with_indices(len(lens), sum(lens), l_ext=2, h_q=8, h_kv=1, d=128)
     plan = va.verify_attn_plan(va.make_desc(**meta, split_tokens=128), 2, 256)
-    assert plan.split_tokens == 128
-    assert _fitted_units(lens, 128, plan.range_slots) == 2
+    assert plan.mode == 2 and plan.split_tokens == 128
+    assert sum(-(-n // 128) for n in lens) <= plan.range_slots
 
 
 def test_pages_split_rule_mode():

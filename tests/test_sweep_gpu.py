@@ -6,19 +6,17 @@ sequences, or uniform multiples of 64, the shape whose ranges start where the
 prefix pass copies its first indices before reading kv_indptr), l_ext, the GQA
 ratio, the head dim, the pool dtype, a contiguous or scattered pool and the
 split mode.  Sizes stay small enough for the oracle to finish in about a
-second per case.  Tolerances as in test_parity_gpu.py.
+second per case.  Tolerances (elementwise and relative L2) from tests/parity.py.
 """
 import numpy as np
 import pytest
 import torch
 
 import oracle
+from parity import BF16_TOL, FP8_TOL, assert_close
 from speculative_decoding_attention_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
-
-BF16_TOL = dict(atol=2e-2, rtol=1e-2)
-FP8_TOL = dict(atol=3e-2, rtol=1e-2)
 
 
 @pytest.fixture(scope="module")
@@ -71,9 +69,4 @@ def test_random_shape(va, seed):
     torch.cuda.synchronize()
     ref = oracle.verify_attn(p.q, p.k_ext, p.v_ext, p.k_buf, p.v_buf, p.qo_indptr, p.kv_indptr,
                              p.kv_indices, p.sm_scale, p.k_scale, p.v_scale)
-    tol = FP8_TOL if c["fp8"] else BF16_TOL
-    g = out.float().cpu().double().numpy()
-    assert np.isfinite(g).all()
-    err = np.abs(g - ref)
-    bad = err > tol["atol"] + tol["rtol"] * np.abs(ref)
-    assert not bad.any(), "%d/%d out of tolerance, max abs err %.3e" % (int(bad.sum()), bad.size, float(err.max()))
+    assert_close(out, ref, FP8_TOL if c["fp8"] else BF16_TOL, p.name)
