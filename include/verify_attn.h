@@ -178,6 +178,26 @@ VA_API int verify_attn_run(const void *q, const void *k_ext, const void *v_ext,
                            const va_desc_t *desc, void *workspace, size_t workspace_bytes,
                            void *stream);
 
+/* verify_attn_run without a workspace, for callers that cannot allocate
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the partial outputs and log-sum-exps live in a device array
+ * the library owns, 32 MiB per GPU (kept until the process ends), instead of
+ * the caller's workspace.  Arguments, results and errors as for
+ * verify_attn_run; a call whose plan needs more than the array holds
+ * (plan.workspace_bytes > 32 MiB: e.g. several hundred sequences of many
+ * query rows) returns VA_ERR_WORKSPACE and launches nothing.  No call
+ * allocates: the array's address on a device is resolved once, by the first
+ * call on that device (make that call outside graph capture).  Every call on
+ * a GPU shares that GPU's array and leaves its contents behind; calls that
+ * overlap in time on one GPU (different streams, or different threads) race
+ * on it and give undefined results. */
+VA_API int verify_attn_run_noalloc(const void *q, const void *k_ext, const void *v_ext,
+                                   const void *k_buf, const void *v_buf,
+                                   const int32_t *qo_indptr, const int32_t *kv_indptr,
+                                   const int64_t *kv_indices, int32_t l_ext,
+                                   float sm_scale, float k_scale, float v_scale, void *out,
+                                   const va_desc_t *desc, void *stream);
+
 /* Prefix pass only (the pages' _verify_prefix_stage1): writes, for every range
  * and query row, the v_scale-multiplied normalised partial output (bf16) and
  * its natural log-sum-exp into the workspace; an empty range writes output 0

@@ -29,7 +29,8 @@ DEVICE = ["-x", "hip", "--offload-arch=" + ARCH,
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-mllvm", "-amdgpu-kernarg-preload-count=10"]
 
-SOURCES = ["va_kernels.hip", "va_aux.hip", "va_plan.cpp", "va_api.cpp", "va_aux_api.cpp"]
+SOURCES = ["va_kernels.hip", "va_aux.hip", "va_noalloc.hip", "va_plan.cpp", "va_api.cpp",
+           "va_aux_api.cpp"]
 
 
 def hipcc() -> str:

@@ -277,6 +277,43 @@ VA_API int verify_attn_run(const void *q, const void *k_ext, const void *v_ext, 
                             workspace, stream);
 }
 
+VA_API int verify_attn_run_noalloc(const void *q, const void *k_ext, const void *v_ext, const void *k_buf,
+                                   const void *v_buf, const int32_t *qo_indptr, const int32_t *kv_indptr,
+                                   const int64_t *kv_indices, int32_t l_ext, float sm_scale, float k_scale,
+                                   float v_scale, void *out, const va_desc_t *desc, void *stream)
+{
+    int rc = va::check_desc(desc, l_ext);  // host checks first: no device query on bad input
+    if (rc != VA_OK)
+        return rc;
+    const void *ptrs[9] = {q, k_ext, v_ext, k_buf, v_buf, qo_indptr, kv_indptr,
+                           desc->num_kv_indices > 0 ? (const void *)kv_indices : (const void *)q, out};
+    if ((rc = va::check_ptrs(ptrs, 9)) != VA_OK)
+        return rc;
+    const void *al[6] = {q, k_ext, v_ext, k_buf, v_buf, out};
+    if ((rc = va::check_align(al, 6)) != VA_OK)
+        return rc;
+    if ((rc = va::check_scales(sm_scale, k_scale, v_scale)) != VA_OK)
+        return rc;
+    va_plan_t plan;
+    if ((rc = va::make_plan(desc, l_ext, 0, &plan)) != VA_OK)
+        return rc;
+    if (plan.workspace_bytes > va::kNoAllocScratchBytes) {
+        va::set_error("the call needs %zu bytes of partials; verify_attn_run_noalloc holds at most %zu "
+                      "(use verify_attn_run with a workspace)",
+                      plan.workspace_bytes, va::kNoAllocScratchBytes);
+        return VA_ERR_WORKSPACE;
+    }
+    void *ws = nullptr;
+    if ((rc = va::noalloc_scratch(&ws)) != VA_OK)
+        return rc;
+    rc = va::prefix_impl(q, k_buf, v_buf, qo_indptr, kv_indptr, kv_indices, l_ext, sm_scale, k_scale,
+                         v_scale, desc, plan, ws, stream);
+    if (rc != VA_OK)
+        return rc;
+    return va::combine_impl(q, k_ext, v_ext, qo_indptr, kv_indptr, l_ext, sm_scale, out, desc, plan, ws,
+                            stream);
+}
+
 VA_API int verify_attn_combine_tree(const void *q, const void *k_ext, const void *v_ext,
                                     const int32_t *qo_indptr, const int32_t *kv_indptr, int32_t l_ext,
                                     float sm_scale, const uint8_t *custom_mask, const int64_t *mask_indptr,

@@ -31,6 +31,10 @@ constexpr int prefix_resident_per_cu(int qblocks) { return qblocks == 1 ? 2 : 1;
 constexpr int kMaxTreeDrafts = 64;
 // Smallest range the heuristic chooses; ranges are multiples of this.
 constexpr int kSplitQuantum = 64;
+// Size of the library-owned device array verify_attn_run_noalloc keeps its
+// partials in (va_noalloc.hip): the headline and 64k-prefix workloads need
+// 8.5 MB of it on MI355X.
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
 
 // Prefix tokens per LDS tile: as many as keep K+V of one tile within 32 KB of
 // raw pool bytes, at most 128 (bf16 D=256: 32; fp8 D=128: 128).
@@ -125,6 +129,9 @@ const char *hip_error_string(int err);
 int check_desc(const va_desc_t *d, int32_t l_ext);
 int make_plan(const va_desc_t *d, int32_t l_ext, int32_t num_cus, va_plan_t *plan);
 int current_device_cus(int32_t *cus);
+// Address of the current device's copy of the verify_attn_run_noalloc array
+// (va_noalloc.hip), resolved once per device.
+int noalloc_scratch(void **ptr);
 void set_error(const char *fmt, ...);
 void clear_error();
 

@@ -66,6 +66,7 @@ def _load():
     lib.verify_attn_plan.argtypes = [DP, I32, I32, ctypes.POINTER(VaPlan)]
     lib.verify_attn_workspace_bytes.argtypes = [DP, I32, I32, ctypes.POINTER(SZ)]
     lib.verify_attn_run.argtypes = [P, P, P, P, P, P, P, P, I32, F, F, F, P, DP, P, SZ, P]
+    lib.verify_attn_run_noalloc.argtypes = [P, P, P, P, P, P, P, P, I32, F, F, F, P, DP, P]
     lib.verify_attn_prefix.argtypes = [P, P, P, P, P, P, I32, F, F, F, DP, P, SZ, P]
     lib.verify_attn_combine.argtypes = [P, P, P, P, P, I32, F, P, DP, P, SZ, P]
     lib.verify_attn_run_paged.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_int64, I32, I32, F, F, F, P, DP,
@@ -76,7 +77,7 @@ def _load():
     lib.verify_attn_append_kv.argtypes = [P, P, P, ctypes.c_int64, F, F, P, P, DP, P]
     lib.verify_attn_build_kv_indices.argtypes = [P, ctypes.c_int64, P, P, P, I32, ctypes.c_int64, P, P, P]
     for name in ("verify_attn_check", "verify_attn_plan", "verify_attn_workspace_bytes",
-                 "verify_attn_run", "verify_attn_prefix", "verify_attn_combine",
+                 "verify_attn_run", "verify_attn_run_noalloc", "verify_attn_prefix", "verify_attn_combine",
                  "verify_attn_run_tree", "verify_attn_combine_tree", "verify_attn_append_kv",
                  "verify_attn_run_paged", "verify_attn_prefix_paged",
                  "verify_attn_build_kv_indices",
@@ -208,6 +209,27 @@ def verify_attn_run(q, k_ext, v_ext, k_buf, v_buf, qo_indptr, kv_indptr, kv_indi
         float(sm_scale), float(k_scale), float(v_scale), _ptr(out), ctypes.byref(desc),
         _ptr(workspace), workspace.numel(), _stream(stream))
     _ok(rc, "verify_attn_run")
+    return out
+
+
+def verify_attn_run_noalloc(q, k_ext, v_ext, k_buf, v_buf, qo_indptr, kv_indptr, kv_indices, l_ext,
+                            sm_scale=None, k_scale=1.0, v_scale=1.0, out=None, split_tokens=0,
+                            n_splits=0, stream=None, desc=None):
+    """As verify_attn_run with the partials in the library's own device array
+    (no workspace argument; the library allocates nothing).  ``out`` should be
+    given by callers that cannot allocate."""
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(q.shape[2])
+    if out is None:
+        out = torch.empty(q.shape[0], q.shape[1], v_ext.shape[2], dtype=q.dtype, device=q.device)
+    bs = qo_indptr.shape[0] - 1
+    if desc is None:
+        desc = make_desc(q, k_ext, v_ext, k_buf, v_buf, kv_indices, out, bs, split_tokens, n_splits)
+    rc = _lib.verify_attn_run_noalloc(
+        _ptr(q), _ptr(k_ext), _ptr(v_ext), _ptr(k_buf), _ptr(v_buf), _ptr(qo_indptr),
+        _ptr(kv_indptr), _ptr(kv_indices) if kv_indices.numel() else 0, int(l_ext),
+        float(sm_scale), float(k_scale), float(v_scale), _ptr(out), ctypes.byref(desc), _stream(stream))
+    _ok(rc, "verify_attn_run_noalloc")
     return out
 
 
