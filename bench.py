@@ -76,16 +76,20 @@ def recorded_traffic(workload):
 
 
 class Runner:
-    """Pre-marshalled arguments for the two C entry points of one replica."""
+    """Pre-marshalled arguments for the two C entry points of one replica.
+    ``kv_indices`` may be given to pass a longer buffer whose first
+    ``sum n_b`` entries are the replica's (a capacity-sized buffer, as under
+    graph capture)."""
 
-    def __init__(self, va, p, workspace, out):
+    def __init__(self, va, p, workspace, out, kv_indices=None):
         import ctypes
-        self.va, self.p, self.ws, self.out = va, p, workspace, out
-        self.desc = va.make_desc(p.q, p.k_ext, p.v_ext, p.k_buf, p.v_buf, p.kv_indices, out, p.bs)
+        idx = p.kv_indices if kv_indices is None else kv_indices
+        self.va, self.p, self.ws, self.out, self.idx = va, p, workspace, out, idx
+        self.desc = va.make_desc(p.q, p.k_ext, p.v_ext, p.k_buf, p.v_buf, idx, out, p.bs)
         self.lib = va.lib()
         F = ctypes.c_float
         self.pre_args = (p.q.data_ptr(), p.k_buf.data_ptr(), p.v_buf.data_ptr(), p.qo_indptr.data_ptr(),
-                         p.kv_indptr.data_ptr(), p.kv_indices.data_ptr(), p.l_ext, F(p.sm_scale),
+                         p.kv_indptr.data_ptr(), idx.data_ptr(), p.l_ext, F(p.sm_scale),
                          F(p.k_scale), F(p.v_scale), ctypes.byref(self.desc), workspace.data_ptr(),
                          workspace.numel())
         self.com_args = (p.q.data_ptr(), p.k_ext.data_ptr(), p.v_ext.data_ptr(), p.qo_indptr.data_ptr(),
@@ -124,7 +128,7 @@ def timed_loop(torch, body, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
-def time_workload(torch, va, W, name, steps, warmup, replicas, seed0=1000):
+def time_workload(torch, va, W, name, steps, warmup, replicas, seed0=1000, capacity_factor=0):
     dev = torch.device("cuda", 0)
     make = W.CONFIGS[name]
     probs = [make(device=dev, seed=seed0 + r) for r in range(replicas)]
@@ -177,23 +181,59 @@ def time_workload(torch, va, W, name, steps, warmup, replicas, seed0=1000):
     ms_warm = timed_loop(torch, warm_step, steps, warmup)
 
     # ---- graph replay: one captured step per replica ----
-    graphs = []
-    try:
+    def capture(runner_list, steps_per_graph):
+        """One graph per runner list entry, each holding `steps_per_graph`
+        steps (rotating through the replicas from that entry on)."""
+        out_graphs = []
         cap = torch.cuda.Stream()
         cap.wait_stream(stream)
         with torch.cuda.stream(cap):
-            for r in runners:
+            for j in range(len(runner_list)):
                 g = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g, stream=cap):
                     cs = torch.cuda.current_stream().cuda_stream
-                    r.prefix(cs)
-                    r.combine(cs)
-                graphs.append(g)
+                    for k in range(steps_per_graph):
+                        r = runner_list[(j + k) % len(runner_list)]
+                        r.prefix(cs)
+                        r.combine(cs)
+                out_graphs.append(g)
         stream.wait_stream(cap)
         torch.cuda.synchronize()
-        ms_graph = timed_loop(torch, lambda i: graphs[i % replicas].replay(), steps, warmup)
+        return out_graphs
+
+    def graph_loop(graphs, steps_per_graph):
+        launches = max(1, steps // steps_per_graph)
+        for i in range(max(1, warmup // steps_per_graph)):
+            graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for i in range(launches):
+            graphs[i % len(graphs)].replay()
+        e1.record(stream)
+        host_us = (time.perf_counter() - t0) * 1e6 / launches
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (launches * steps_per_graph), host_us
+
+    ms_graph = ms_graph20 = ms_graph_cap = None
+    host_graph_us = host_graph20_us = None
+    try:
+        ms_graph, host_graph_us = graph_loop(capture(runners, 1), 1)
+        # 20 steps in one graph: the host launches once per 20 steps
+        ms_graph20, host_graph20_us = graph_loop(capture(runners, 20), 20)
+        if capacity_factor:
+            # kv_indices a buffer of capacity_factor x the batch's tokens (the
+            # graph mode of the pages' backend); the plan is made for its length
+            caps = []
+            for r in runners:
+                buf = torch.zeros(capacity_factor * r.p.kv_indices.numel(), dtype=torch.int64, device=dev)
+                buf[:r.p.kv_indices.numel()].copy_(r.p.kv_indices)
+                caps.append(Runner(va, r.p, ws, out, kv_indices=buf))
+            need = max(va.verify_attn_workspace_bytes(r.desc, r.p.l_ext) for r in caps)
+            assert need <= ws.numel(), "capacity plan needs a larger workspace"
+            ms_graph_cap, _ = graph_loop(capture(caps, 1), 1)
     except Exception as exc:  # report, never hide
-        ms_graph = None
         print("graph replay timing failed: %r" % (exc,), file=sys.stderr)
 
     us = lambda ms: round(ms * 1e3, 3)
@@ -209,6 +249,11 @@ def time_workload(torch, va, W, name, steps, warmup, replicas, seed0=1000):
         us_step_warm=us(ms_warm), gbs_warm=kv_bytes / (ms_warm * 1e-3) / 1e9,
         us_step_graph=us(ms_graph) if ms_graph else None,
         gbs_graph=(kv_bytes / (ms_graph * 1e-3) / 1e9) if ms_graph else None,
+        host_us_per_graph_launch=round(host_graph_us, 2) if host_graph_us else None,
+        us_step_graph20=us(ms_graph20) if ms_graph20 else None,
+        host_us_per_graph20_launch=round(host_graph20_us, 2) if host_graph20_us else None,
+        us_step_graph_capacity=us(ms_graph_cap) if ms_graph_cap else None,
+        capacity_factor=capacity_factor or None,
     )
 
 
@@ -399,7 +444,7 @@ def main():
     torch.cuda.set_device(0)
     calibration_copy(torch)
     torch.cuda.synchronize()
-    head = time_workload(torch, va, W, args.workload, args.steps, args.warmup, args.replicas)
+    head = time_workload(torch, va, W, args.workload, args.steps, args.warmup, args.replicas, capacity_factor=4)
     print("[bench] %s: %.2f us/step (%.1f GB/s), prefix kernel %.2f us with per-launch events "
           "(%.1f GB/s), %.2f us back to back; combine %.2f us"
           % (head["name"], head["us_step"], head["gbs"], head["prefix_us_mean"], head["prefix_gbs"],
@@ -407,7 +452,8 @@ def main():
 
     secondary = {}
     if not args.quick:
-        for name, reps in (("b4_64k", 1), ("fp8_ragged", 8), ("decode_b64", 2), ("draft_extend_b16", 8)):
+        for name, reps in (("b4_64k", 1), ("fp8_ragged", 8), ("decode_b64", 2), ("decode_b512", 1),
+                           ("draft_extend_b16", 8)):
             r = time_workload(torch, va, W, name, max(20, args.steps // 4), max(5, args.warmup // 4), reps,
                               seed0=2000)
             secondary[name] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in r.items()
@@ -486,7 +532,11 @@ def main():
             "combine_us_mean": head["combine_us_mean"],
             "warm_cache": {"us_per_call": head["us_step_warm"], "gbs": round(head["gbs_warm"], 2)},
             "graph_replay": {"us_per_call": head["us_step_graph"],
-                             "gbs": round(head["gbs_graph"], 2) if head["gbs_graph"] else None},
+                             "gbs": round(head["gbs_graph"], 2) if head["gbs_graph"] else None,
+                             "host_us_per_launch": head["host_us_per_graph_launch"],
+                             "twenty_steps_per_graph_us_per_call": head["us_step_graph20"],
+                             "host_us_per_twenty_step_launch": head["host_us_per_graph20_launch"],
+                             "kv_indices_capacity_4x_us_per_call": head["us_step_graph_capacity"]},
             "secondary": secondary,
             "around_verify": extensions,
         },

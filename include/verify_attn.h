@@ -124,6 +124,7 @@ typedef struct {
     int64_t combine_blocks;  /* grid of the combine kernel (one 64-thread workgroup per output row) */
     size_t workspace_bytes;  /* bytes of workspace the two passes need */
     size_t partial_bytes;    /* of which: bf16 partial outputs (the fp32 log-sum-exps follow) */
+    size_t table_offset;     /* then, from this offset: each sequence's first range and range count */
 } va_plan_t;
 
 /* Validate a descriptor (host only; no HIP call).

@@ -85,6 +85,7 @@ int prefix_impl(const void *q, const void *k_buf, const void *v_buf, const int32
     p.kv_indices = kv_indices;
     p.part_o = (uint16_t *)workspace;
     p.part_lse = (float *)((char *)workspace + plan.partial_bytes);
+    p.seq_ranges = (int32_t *)((char *)workspace + plan.table_offset);
     const int eb = desc->kv_dtype == VA_DTYPE_FP8_E4M3FN ? 1 : 2;
     p.q_s0 = desc->q_stride[0];
     p.q_s1 = desc->q_stride[1];
@@ -129,6 +130,7 @@ int combine_impl(const void *q, const void *k_ext, const void *v_ext, const int3
     c.kv_indptr = kv_indptr;
     c.part_o = (const uint16_t *)workspace;
     c.part_lse = (const float *)((const char *)workspace + plan.partial_bytes);
+    c.seq_ranges = (const int32_t *)((const char *)workspace + plan.table_offset);
     c.out = (uint16_t *)out;
     c.q_s0 = desc->q_stride[0];
     c.q_s1 = desc->q_stride[1];
@@ -147,8 +149,12 @@ int combine_impl(const void *q, const void *k_ext, const void *v_ext, const int3
     c.mode = plan.mode;
     c.split_tokens = plan.split_tokens > 0 ? plan.split_tokens : 1;
     c.n_splits = plan.n_splits > 0 ? plan.n_splits : 1;
-    c.range_cap = (int32_t)plan.range_slots;
-    int e = launch_combine(c, desc->head_dim, plan.combine_blocks, stream);
+    // preload depths from static shapes: ranges per sequence the grid allows
+    // on average (a batch may exceed it; the kernel then loops) and draft rows
+    const int64_t per_seq = plan.mode == 1 ? plan.n_splits : (plan.range_slots + desc->bs - 1) / desc->bs;
+    const int pre = per_seq <= 8 ? 8 : 32;
+    const int pre_d = l_ext == 1 ? 1 : (l_ext <= 4 ? 4 : 8);
+    int e = launch_combine(c, desc->head_dim, pre, pre_d, plan.combine_blocks, stream);
     if (e != 0) {
         set_error("combine kernel launch: %s", hip_error_string(e));
         return VA_ERR_DEVICE;

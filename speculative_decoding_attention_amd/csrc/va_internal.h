@@ -60,6 +60,7 @@ struct PrefixParams {
     int32_t page_size;
     uint16_t *part_o;  // [range_slots * h_kv, rows, D] bf16 (round to nearest even)
     float *part_lse;   // [range_slots * h_kv, rows]    fp32 (natural log)
+    int32_t *seq_ranges;  // [bs][2]: first range and range count of each sequence (modes 0, 2)
     int64_t q_s0, q_s1;        // elements
     uint32_t kb_s0, vb_s0;     // pool row strides, bytes (< 2^32, checked on the host)
     int64_t kb_s1, vb_s1;      // pool head strides, bytes
@@ -78,6 +79,7 @@ struct CombineParams {
     const int32_t *kv_indptr;
     const uint16_t *part_o;
     const float *part_lse;
+    const int32_t *seq_ranges;  // written by the prefix pass (modes 0, 2)
     uint16_t *out;
     const uint8_t *mask;          // tree mask bytes, or NULL for the causal draft block
     const int64_t *mask_indptr;   // [bs + 1] byte offsets of each sequence's mask
@@ -85,7 +87,6 @@ struct CombineParams {
     float sm_scale;
     int32_t bs, h_kv, group, l_ext, rows;
     int32_t mode, split_tokens, n_splits;
-    int32_t range_cap;  // modes 0, 2: ranges per KV head the prefix grid holds
 };
 
 // Threads per workgroup of the append and kv_indices kernels (va_aux.hip).
@@ -122,7 +123,8 @@ int launch_build_kv_indices(const BuildIndicesParams &p, void *stream);
 // Launchers (defined in va_kernels.hip).  Return a hipError_t value.
 int launch_prefix(const PrefixParams &p, int head_dim, bool kv_fp8, int qblocks,
                   int64_t blocks, void *stream);
-int launch_combine(const CombineParams &p, int head_dim, int64_t blocks, void *stream);
+// pre: partial rows per load batch (8 or 32); pre_d: draft rows preloaded (1, 4 or 8)
+int launch_combine(const CombineParams &p, int head_dim, int pre, int pre_d, int64_t blocks, void *stream);
 const char *hip_error_string(int err);
 
 // Host-side validation and planning (defined in va_plan.cpp).

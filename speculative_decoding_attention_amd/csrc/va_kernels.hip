@@ -164,6 +164,7 @@ struct Range {
     int32_t end;
     int32_t kv_base;  // kv_indptr[b]
     int32_t qo;       // qo_indptr[b]
+    int32_t seq_ranges;  // ranges of sequence b (modes 0, 2)
     bool valid;
 };
 
@@ -275,7 +276,7 @@ __device__ __forceinline__ uint32_t range_units(const int32_t *kv_indptr, const 
 __device__ __forceinline__ Range locate_range(const int32_t *kv_indptr, const int32_t *qo_indptr,
                                               int32_t bs, int32_t n_splits, int64_t cidx)
 {
-    Range r = {0, 0, 0, 0, 0, false};
+    Range r = {0, 0, 0, 0, 0, 0, false};
     const int64_t b = cidx / n_splits;
     if (b >= bs)
         return r;
@@ -312,7 +313,7 @@ __device__ __forceinline__ Range locate_split_range(const int32_t *kv_indptr, co
                                                     int32_t bs, uint32_t k, int64_t cidx,
                                                     const SeqGroup<NC> &first)
 {
-    Range r = {0, 0, 0, 0, 0, false};
+    Range r = {0, 0, 0, 0, 0, 0, false};
     const int32_t c_tok = (int32_t)(k << 6);
     int64_t cum = 0;
     for (int32_t b0 = 0; b0 < bs; b0 += 64 * NC) {
@@ -332,6 +333,7 @@ __device__ __forceinline__ Range locate_split_range(const int32_t *kv_indptr, co
                 r.end = min(r.start + c_tok, lane_i((int32_t)n, h));
                 r.kv_base = lane_i(g.k0[c], h);
                 r.qo = lane_i(g.q0[c], h);
+                r.seq_ranges = lane_i(nch, h);
                 r.valid = true;
                 return r;
             }
@@ -339,34 +341,6 @@ __device__ __forceinline__ Range locate_split_range(const int32_t *kv_indptr, co
         }
     }
     return r;
-}
-
-// First partial slot and slot count of sequence b (whole-wave call).
-template <int NC>
-__device__ __forceinline__ void ranges_of(const int32_t *kv_indptr, const int32_t *qo_indptr, int32_t bs,
-                                          int32_t mode, int32_t split_tokens, int32_t n_splits, int32_t cap,
-                                          int32_t b, const SeqGroup<NC> &first, int32_t *base, int32_t *count)
-{
-    if (mode == 1) {
-        *base = b * n_splits;
-        *count = n_splits;
-        return;
-    }
-    const uint32_t k = range_units<NC>(kv_indptr, qo_indptr, bs, mode, split_tokens, cap, first);
-    const int32_t lane = (int32_t)(threadIdx.x & 63);
-    uint32_t acc = 0, own = 0;
-    for (int32_t b0 = 0; b0 <= b; b0 += 64 * NC) {
-        const SeqGroup<NC> g = b0 == 0 ? first : load_group<NC>(kv_indptr, qo_indptr, bs, b0);
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            const int32_t bb = b0 + 64 * c + lane;
-            const uint32_t nch = ranges_for(seq_len(g, c, b0, bs), k);
-            own = bb == b ? nch : own;
-            acc += bb < b ? nch : 0u;
-        }
-    }
-    *base = wave_sum_i((int32_t)acc);
-    *count = lane_i((int32_t)own, __builtin_amdgcn_readfirstlane(b & 63));
 }
 
 // ----------------------------------------------------------- prefix kernel ---
@@ -673,6 +647,10 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64, 2) void prefix_kernel(
         wait_vm<0>();  // early index copies of a surplus slot of the static grid
         return;        // (never read by the combine pass)
     }
+    // the first range of each sequence records where the sequence's ranges
+    // sit, for the combine pass (modes 0 and 2; mode 1 needs no table)
+    if (mode != 1 && kvh == 0 && rc == 0 && rg.start == 0 && tid == 0)
+        ((i32x2_t *)p.seq_ranges)[rg.b] = i32x2_t{(int32_t)cidx, rg.seq_ranges};
     const int64_t slot = cidx * h_kv + kvh;
     uint16_t *po = p.part_o + slot * (int64_t)rows * D;
     float *pl = p.part_lse + slot * (int64_t)rows;
@@ -1094,14 +1072,18 @@ __device__ __forceinline__ void load_bf16_row(const uint16_t *src, float (&dst)[
     }
 }
 
-template <int D>
+// PRE (partial rows per load batch) and PRE_D (draft rows loaded in the
+// second round) are the host's choice from static shapes: every load of a
+// batch is issued, and lanes past the sequence's ranges or draft rows re-read
+// a valid row, so depths beyond what the batch needs only move duplicate
+// bytes (a decode step has one or two ranges and one draft row per sequence).
+template <int D, int PRE, int PRE_D>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     const int32_t *kv_indptr, const int32_t *qo_indptr, int32_t bs, int32_t mode, int32_t split_tokens,
     int32_t n_splits, int32_t h_kv, int32_t rows, const CombineParams p)
 {  // leading arguments preloaded into SGPRs, as for the prefix kernel
     constexpr int VPL = D / 64;  // elements of D / Dv per lane
-    constexpr int PRE = 32;      // partial outputs per load batch (the first in the second load round)
-    constexpr int PRE_D = 8;     // draft rows loaded in the first round
+    static_assert(PRE >= 1 && PRE <= 64 && PRE_D >= 1 && PRE_D <= 64, "preload depths");
 
     const int lane = threadIdx.x & 63;
     // the plan keeps bs * h_kv * rows below 2^31
@@ -1119,27 +1101,19 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
 
     // ---- first load round: where this sequence's rows and ranges are ----
     const int qo = qo_indptr[b];
-    auto pin_args = [&]() {
-        asm volatile("" ::"s"(p.q), "s"(p.k_ext), "s"(p.v_ext), "s"(p.part_o), "s"(p.part_lse), "s"(p.q_s0),
-                     "s"(p.q_s1), "s"(p.ke_s0), "s"(p.ke_s1), "s"(p.ve_s0), "s"(p.ve_s1), "s"(p.group),
-                     "s"(p.l_ext), "s"(p.range_cap)
-                     : "memory");
-    };
-    int32_t base, count;
-    if (bs <= 64) {
-        const SeqGroup<1> first = load_group<1>(kv_indptr, qo_indptr, bs, 0);
-        pin_args();
-        ranges_of<1>(kv_indptr, qo_indptr, bs, mode, split_tokens, n_splits, p.range_cap, b, first, &base, &count);
-    } else {
-        const SeqGroup<8> first = load_group<8>(kv_indptr, qo_indptr, bs, 0);
-        pin_args();
-        ranges_of<8>(kv_indptr, qo_indptr, bs, mode, split_tokens, n_splits, p.range_cap, b, first, &base, &count);
-    }
+    // modes 0 and 2: the prefix pass recorded the sequence's first range and
+    // range count (only for sequences with a prefix; an empty one has none)
+    const int32_t k0 = kv_indptr[b], k1 = kv_indptr[b + 1];
+    const i32x2_t tab = ((const i32x2_t *)p.seq_ranges)[b];
+    asm volatile("" ::"s"(p.q), "s"(p.k_ext), "s"(p.v_ext), "s"(p.part_o), "s"(p.part_lse), "s"(p.q_s0),
+                 "s"(p.q_s1), "s"(p.ke_s0), "s"(p.ke_s1), "s"(p.ve_s0), "s"(p.ve_s1), "s"(p.group), "s"(p.l_ext)
+                 : "memory");
+    const int32_t base = mode == 1 ? b * n_splits : tab[0];
+    const int32_t count = mode == 1 ? n_splits : (k1 > k0 ? tab[1] : 0);
     const int L = p.l_ext;
     int64_t mrow = 0;  // this row's tree-mask bytes for the draft keys
     if (p.mask)
-        mrow = p.mask_indptr[b] + (int64_t)di * (kv_indptr[b + 1] - kv_indptr[b] + L) +
-               (kv_indptr[b + 1] - kv_indptr[b]);
+        mrow = p.mask_indptr[b] + (int64_t)di * (k1 - k0 + L) + (k1 - k0);
 
     // ---- second load round: log-sum-exps, partial outputs, query row, draft rows ----
     const int64_t lse_step = (int64_t)p.h_kv * p.rows;  // next range, same head and row
@@ -1327,16 +1301,36 @@ int launch_prefix(const PrefixParams &p, int head_dim, bool kv_fp8, int qblocks,
     }
 }
 
-int launch_combine(const CombineParams &p, int head_dim, int64_t blocks, void *stream)
+template <int D, int PRE>
+static void launch_combine_d(const CombineParams &p, int pre_d, dim3 grid, dim3 block, hipStream_t s)
+{
+#define VA_COMBINE_ARGS p.kv_indptr, p.qo_indptr, p.bs, p.mode, p.split_tokens, p.n_splits, p.h_kv, p.rows, p
+    if (pre_d == 1)
+        hipLaunchKernelGGL((combine_kernel<D, PRE, 1>), grid, block, 0, s, VA_COMBINE_ARGS);
+    else if (pre_d == 4)
+        hipLaunchKernelGGL((combine_kernel<D, PRE, 4>), grid, block, 0, s, VA_COMBINE_ARGS);
+    else
+        hipLaunchKernelGGL((combine_kernel<D, PRE, 8>), grid, block, 0, s, VA_COMBINE_ARGS);
+#undef VA_COMBINE_ARGS
+}
+
+template <int D>
+static void launch_combine_pre(const CombineParams &p, int pre, int pre_d, dim3 grid, dim3 block, hipStream_t s)
+{
+    if (pre == 8)
+        launch_combine_d<D, 8>(p, pre_d, grid, block, s);
+    else
+        launch_combine_d<D, 32>(p, pre_d, grid, block, s);
+}
+
+int launch_combine(const CombineParams &p, int head_dim, int pre, int pre_d, int64_t blocks, void *stream)
 {
     hipStream_t s = (hipStream_t)stream;
     dim3 grid((unsigned)blocks), block(kCombineThreads);
     switch (head_dim) {
-#define VA_COMBINE_ARGS p.kv_indptr, p.qo_indptr, p.bs, p.mode, p.split_tokens, p.n_splits, p.h_kv, p.rows, p
-    case 64: hipLaunchKernelGGL((combine_kernel<64>), grid, block, 0, s, VA_COMBINE_ARGS); break;
-    case 128: hipLaunchKernelGGL((combine_kernel<128>), grid, block, 0, s, VA_COMBINE_ARGS); break;
-    default: hipLaunchKernelGGL((combine_kernel<256>), grid, block, 0, s, VA_COMBINE_ARGS); break;
-#undef VA_COMBINE_ARGS
+    case 64: launch_combine_pre<64>(p, pre, pre_d, grid, block, s); break;
+    case 128: launch_combine_pre<128>(p, pre, pre_d, grid, block, s); break;
+    default: launch_combine_pre<256>(p, pre, pre_d, grid, block, s); break;
     }
     return (int)hipGetLastError();
 }

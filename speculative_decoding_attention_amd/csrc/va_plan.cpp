@@ -195,8 +195,13 @@ int make_plan(const va_desc_t *d, int32_t l_ext, int32_t num_cus, va_plan_t *pla
         return fail(VA_ERR_SIZE, "grid too large (%lld prefix workgroups)", (long long)p.prefix_blocks);
     const int64_t o_bytes = align_up(slots * rows * d->v_head_dim * 2, 256);  // bf16 partials
     const int64_t l_bytes = align_up(slots * rows * 4, 256);
+    // each sequence's first range and range count (the prefix pass writes
+    // them for the combine pass, which loads its sequence's entry
+    // unconditionally, so the table is there even when no prefix pass runs)
+    const int64_t t_bytes = align_up((int64_t)d->bs * 8, 256);
     p.partial_bytes = (size_t)o_bytes;
-    p.workspace_bytes = (size_t)(o_bytes + l_bytes);
+    p.table_offset = (size_t)(o_bytes + l_bytes);
+    p.workspace_bytes = (size_t)(o_bytes + l_bytes + t_bytes);
     *plan = p;
     clear_error();
     return VA_OK;
@@ -251,6 +256,6 @@ VA_API const char *verify_attn_strerror(int code)
 
 VA_API const char *verify_attn_last_error(void) { return va::last_error(); }
 
-VA_API int verify_attn_version(void) { return 200; }
+VA_API int verify_attn_version(void) { return 300; }
 
 }  // extern "C"

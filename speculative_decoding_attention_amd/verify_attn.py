@@ -47,7 +47,7 @@ class VaPlan(ctypes.Structure):
         ("rows", ctypes.c_int32), ("row_chunks", ctypes.c_int32), ("tile_tokens", ctypes.c_int32),
         ("range_slots", ctypes.c_int64), ("prefix_blocks", ctypes.c_int64),
         ("combine_blocks", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t),
-        ("partial_bytes", ctypes.c_size_t),
+        ("partial_bytes", ctypes.c_size_t), ("table_offset", ctypes.c_size_t),
     ]
 
     def as_dict(self):

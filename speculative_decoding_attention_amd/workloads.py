@@ -214,13 +214,19 @@ def config_b4_64k(device="cpu", seed=5):
 
 
 # Reuse of the same entry point for other modes with a fixed extend length
-# per request: plain decode (l_ext = 1) of a large batch, and the draft model's
+# per request: plain decode (l_ext = 1) of a 64- and a 512-sequence batch, and
+# the draft model's
 # DRAFT_EXTEND_V2 step (num_draft_tokens new tokens per request over the
 # draft-side prefix); both with the headline attention geometry (16/2 heads,
 # D = 256, scattered pool) and seeded ragged prefixes.
 def config_decode_b64(device="cpu", seed=6):
     return make_problem(fp8_prefix_lens(seed, bs=64, lo=2048, hi=6144), 1, 16, 2, 256, 256,
                         pool_factor=2, permute=True, seed=seed, device=device, name="decode_b64")
+
+
+def config_decode_b512(device="cpu", seed=8):
+    return make_problem(fp8_prefix_lens(seed, bs=512, lo=1024, hi=4096), 1, 16, 2, 256, 256,
+                        pool_factor=2, permute=True, seed=seed, device=device, name="decode_b512")
 
 
 def config_draft_extend_b16(device="cpu", seed=7):
@@ -236,5 +242,6 @@ CONFIGS = {
     "fp8_ragged": config_fp8_ragged,
     "b4_64k": config_b4_64k,
     "decode_b64": config_decode_b64,
+    "decode_b512": config_decode_b512,
     "draft_extend_b16": config_draft_extend_b16,
 }

@@ -189,6 +189,19 @@ def test_large_batches(va, bs, l_ext, hq, hkv, d, kv):
     check_full(va, p, split_tokens=128)
 
 
+def test_one_long_sequence_among_short_ones(va):
+    # 40 sequences whose grid averages under 8 ranges each, so the combine
+    # pass preloads 8 partial rows at a time; the 20000-token sequence has
+    # about 157 ranges, so its merge loops over batches of 8 and reloads the
+    # range weights past every 64 ranges
+    lens = [20000] + [10] * 39
+    p = W.make_problem(lens, 4, 16, 2, 256, k_scale=0.5, v_scale=0.25, pool_factor=2, permute=True,
+                       seed=85, name="one long")
+    hint, fit = _hint_and_fit(va, p)
+    assert -(-20000 // fit) > 64
+    check_full(va, p)
+
+
 def test_kv_scales(va):
     check_full(va, W.make_problem([1024, 2048], 4, 16, 2, 256, k_scale=0.5, v_scale=0.25, seed=55,
                                   name="scales"))
