@@ -53,7 +53,7 @@ typedef enum {
     VA_ERR_NULL_ARG = -1,   /* a required pointer is NULL */
     VA_ERR_BATCH = -2,      /* bs < 1 */
     VA_ERR_HEADS = -3,      /* h_q or h_kv < 1, or h_q % h_kv != 0 */
-    VA_ERR_HEAD_DIM = -4,   /* head_dim != v_head_dim or not in {64,128,256} */
+    VA_ERR_HEAD_DIM = -4,   /* head dims not in {64,128,256}, or neither equal nor a factor 2 apart */
     VA_ERR_DTYPE = -5,      /* kv_dtype not a va_dtype_t */
     VA_ERR_EXTEND = -6,     /* l_ext < 1, or q_rows != bs * l_ext (ragged extend) */
     VA_ERR_STRIDE = -7,     /* stride not positive, rows overlap, or row start not 16-B aligned */
@@ -73,6 +73,10 @@ typedef enum {
  *   k_buf  [pool,   h_kv, head_dim]    kv_dtype strides kbuf_stride[0..1]
  *   v_buf  [pool,   h_kv, v_head_dim]  kv_dtype strides vbuf_stride[0..1]
  *   out    [q_rows, h_q,  v_head_dim]  bf16     strides out_stride[0..1]
+ * head_dim and v_head_dim are separate, as verify_splitkv.py keeps them
+ * (VerifySplitKV(..., head_dim, v_head_dim, ...); BLOCK_DV in
+ * _verify_prefix_stage1): both in {64, 128, 256}, equal or one twice the
+ * other.
  * num_kv_indices is the length of kv_indices: a static shape, which may be
  * the capacity of a buffer sized for the largest batch (as a captured graph
  * replays it) rather than the batch's own total; every kv_indptr entry must
@@ -129,7 +133,7 @@ typedef struct {
 
 /* Validate a descriptor (host only; no HIP call).
  * Mirrors can_handle() in verify_splitkv.py, which accepts only causal topk=1
- * verify with a constant extend length: bs >= 1, h_q % h_kv == 0, consistent
+ * verify with a constant extend length: bs >= 1, h_q % h_kv == 0, supported
  * head dims, q_rows == bs * l_ext.  Returns VA_OK or the first failing code. */
 VA_API int verify_attn_check(const va_desc_t *desc, int32_t l_ext);
 

@@ -106,7 +106,7 @@ int prefix_impl(const void *q, const void *k_buf, const void *v_buf, const int32
     p.n_splits = plan.n_splits > 0 ? plan.n_splits : 1;
     p.total_tokens = (int32_t)desc->num_kv_indices;  // < 2^31, checked by the planner
     const int qb = query_blocks_for(plan.rows < kRowChunk ? plan.rows : kRowChunk);
-    int e = launch_prefix(p, desc->head_dim, desc->kv_dtype == VA_DTYPE_FP8_E4M3FN, qb,
+    int e = launch_prefix(p, desc->head_dim, desc->v_head_dim, desc->kv_dtype == VA_DTYPE_FP8_E4M3FN, qb,
                           plan.prefix_blocks, stream);
     if (e != 0) {
         set_error("prefix kernel launch: %s", hip_error_string(e));
@@ -154,7 +154,7 @@ int combine_impl(const void *q, const void *k_ext, const void *v_ext, const int3
     const int64_t per_seq = plan.mode == 1 ? plan.n_splits : (plan.range_slots + desc->bs - 1) / desc->bs;
     const int pre = per_seq <= 8 ? 8 : 32;
     const int pre_d = l_ext == 1 ? 1 : (l_ext <= 4 ? 4 : 8);
-    int e = launch_combine(c, desc->head_dim, pre, pre_d, plan.combine_blocks, stream);
+    int e = launch_combine(c, desc->head_dim, desc->v_head_dim, pre, pre_d, plan.combine_blocks, stream);
     if (e != 0) {
         set_error("combine kernel launch: %s", hip_error_string(e));
         return VA_ERR_DEVICE;

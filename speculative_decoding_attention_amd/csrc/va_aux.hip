@@ -81,7 +81,7 @@ __device__ __forceinline__ void append_row(const uint16_t *src, uint8_t *dst, fl
     }
 }
 
-template <int D, bool FP8>
+template <int D, int DV, bool FP8>
 __global__ __launch_bounds__(kAuxThreads) void append_kernel(const AppendParams p)
 {
     const int lane = threadIdx.x & 63;
@@ -93,8 +93,8 @@ __global__ __launch_bounds__(kAuxThreads) void append_kernel(const AppendParams 
     const int64_t t = p.loc[i];
     append_row<D, FP8>(p.k + i * p.k_s0 + (int64_t)g * p.k_s1, p.k_buf + t * p.kb_s0 + (int64_t)g * p.kb_s1,
                        p.k_scale, lane);
-    append_row<D, FP8>(p.v + i * p.v_s0 + (int64_t)g * p.v_s1, p.v_buf + t * p.vb_s0 + (int64_t)g * p.vb_s1,
-                       p.v_scale, lane);
+    append_row<DV, FP8>(p.v + i * p.v_s0 + (int64_t)g * p.v_s1, p.v_buf + t * p.vb_s0 + (int64_t)g * p.vb_s1,
+                        p.v_scale, lane);
 }
 
 // grid: bs * parts workgroups; part q of request b copies tokens q, q + parts *
@@ -134,20 +134,26 @@ __global__ __launch_bounds__(kAuxThreads) void build_kv_indices_kernel(const Bui
 
 }  // namespace
 
-int launch_append(const AppendParams &p, int head_dim, bool kv_fp8, void *stream)
+int launch_append(const AppendParams &p, int head_dim, int v_head_dim, bool kv_fp8, void *stream)
 {
     hipStream_t s = (hipStream_t)stream;
     const int64_t rows = p.n * p.h_kv;
     dim3 grid((unsigned)((rows + kAuxThreads / 64 - 1) / (kAuxThreads / 64))), block(kAuxThreads);
-#define VA_APPEND(D)                                                                   \
+#define VA_APPEND(D, DV)                                                               \
     if (kv_fp8)                                                                        \
-        hipLaunchKernelGGL((append_kernel<D, true>), grid, block, 0, s, p);            \
+        hipLaunchKernelGGL((append_kernel<D, DV, true>), grid, block, 0, s, p);        \
     else                                                                               \
-        hipLaunchKernelGGL((append_kernel<D, false>), grid, block, 0, s, p);
-    switch (head_dim) {
-    case 64: VA_APPEND(64) break;
-    case 128: VA_APPEND(128) break;
-    default: VA_APPEND(256) break;
+        hipLaunchKernelGGL((append_kernel<D, DV, false>), grid, block, 0, s, p);
+    // the head-dim pairs of the verify kernels (the host checks)
+    switch (head_dim * 1000 + v_head_dim) {
+    case 64064: VA_APPEND(64, 64) break;
+    case 64128: VA_APPEND(64, 128) break;
+    case 128064: VA_APPEND(128, 64) break;
+    case 128128: VA_APPEND(128, 128) break;
+    case 128256: VA_APPEND(128, 256) break;
+    case 256128: VA_APPEND(256, 128) break;
+    case 256256: VA_APPEND(256, 256) break;
+    default: return (int)hipErrorInvalidValue;
     }
 #undef VA_APPEND
     return (int)hipGetLastError();

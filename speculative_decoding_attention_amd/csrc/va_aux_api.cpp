@@ -22,8 +22,9 @@ VA_API int verify_attn_append_kv(const void *k, const void *v, const int64_t *ou
         return VA_ERR_HEADS;
     }
     const int d = desc->head_dim, dv = desc->v_head_dim;
-    if (d != dv || (d != 64 && d != 128 && d != 256)) {
-        set_error("head_dim = %d, v_head_dim = %d; supported: equal and in {64,128,256}", d, dv);
+    if (!supported_head_dims(d, dv)) {
+        set_error("head_dim = %d, v_head_dim = %d; supported: both in {64,128,256}, equal or one twice the other",
+                  d, dv);
         return VA_ERR_HEAD_DIM;
     }
     if (desc->kv_dtype != VA_DTYPE_BF16 && desc->kv_dtype != VA_DTYPE_FP8_E4M3FN) {
@@ -81,7 +82,7 @@ VA_API int verify_attn_append_kv(const void *k, const void *v, const int64_t *ou
     p.vb_s1 = desc->vbuf_stride[1] * eb;
     p.k_scale = k_scale;
     p.v_scale = v_scale;
-    const int e = launch_append(p, d, fp8, stream);
+    const int e = launch_append(p, d, dv, fp8, stream);
     if (e != 0) {
         set_error("append kernel launch: %s", hip_error_string(e));
         return VA_ERR_DEVICE;

@@ -36,11 +36,23 @@ constexpr int kSplitQuantum = 64;
 // 8.5 MB of it on MI355X.
 constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
 
-// Prefix tokens per LDS tile: as many as keep K+V of one tile within 32 KB of
-// raw pool bytes, at most 128 (bf16 D=256: 32; fp8 D=128: 128).
-constexpr int tile_tokens_for(int head_dim, int elem_bytes)
+// Prefix tokens per LDS tile: as many as keep a tile within 32 KB when K and
+// V rows both had the larger head dim, at most 128 (bf16 D=256: 32; fp8
+// D=128: 128).
+constexpr int tile_tokens_for(int head_dim, int v_head_dim, int elem_bytes)
 {
-    return 16384 / (head_dim * elem_bytes) > 128 ? 128 : 16384 / (head_dim * elem_bytes);
+    const int dm = head_dim > v_head_dim ? head_dim : v_head_dim;
+    return 16384 / (dm * elem_bytes) > 128 ? 128 : 16384 / (dm * elem_bytes);
+}
+
+// Head-dim pairs the kernels are built for: both in {64, 128, 256}, equal
+// or one twice the other.
+constexpr bool supported_head_dims(int head_dim, int v_head_dim)
+{
+    const bool d_ok = head_dim == 64 || head_dim == 128 || head_dim == 256;
+    const bool dv_ok = v_head_dim == 64 || v_head_dim == 128 || v_head_dim == 256;
+    return d_ok && dv_ok &&
+           (head_dim == v_head_dim || head_dim == 2 * v_head_dim || v_head_dim == 2 * head_dim);
 }
 
 // 32-row query blocks (MFMA column blocks) per row chunk: 1 or 2.
@@ -117,14 +129,15 @@ struct BuildIndicesParams {
     int32_t bs, parts;               // parts: workgroups per request
 };
 
-int launch_append(const AppendParams &p, int head_dim, bool kv_fp8, void *stream);
+int launch_append(const AppendParams &p, int head_dim, int v_head_dim, bool kv_fp8, void *stream);
 int launch_build_kv_indices(const BuildIndicesParams &p, void *stream);
 
 // Launchers (defined in va_kernels.hip).  Return a hipError_t value.
-int launch_prefix(const PrefixParams &p, int head_dim, bool kv_fp8, int qblocks,
+int launch_prefix(const PrefixParams &p, int head_dim, int v_head_dim, bool kv_fp8, int qblocks,
                   int64_t blocks, void *stream);
 // pre: partial rows per load batch (8 or 32); pre_d: draft rows preloaded (1, 4 or 8)
-int launch_combine(const CombineParams &p, int head_dim, int pre, int pre_d, int64_t blocks, void *stream);
+int launch_combine(const CombineParams &p, int head_dim, int v_head_dim, int pre, int pre_d, int64_t blocks,
+                   void *stream);
 const char *hip_error_string(int err);
 
 // Host-side validation and planning (defined in va_plan.cpp).

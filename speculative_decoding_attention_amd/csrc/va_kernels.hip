@@ -374,24 +374,36 @@ __device__ __forceinline__ void wait_vm()
 // (lgkmcnt 0) before it arrives.  Copies into LDS are covered by wait_vm first.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-template <bool FP8, int D, int NQB>
+// K rows have D elements, V rows DV; the larger of the two sizes the tile and
+// the ring, so each stage holds a K region and a V region of TN rows of the
+// larger row size (the smaller operand leaves the end of its region unused).
+template <bool FP8, int D, int DV, int NQB>
 struct PrefixGeom {
     static constexpr int NW = prefix_waves(NQB);
     static constexpr int E = FP8 ? 1 : 2;               // pool bytes per element
-    static constexpr int ROWB = D * E;                  // pool bytes per K (or V) row
-    static constexpr int TN0 = 16384 / ROWB;
+    static constexpr int DM = D > DV ? D : DV;
+    static constexpr int ROWB_K = D * E;                // pool bytes per K row
+    static constexpr int ROWB_V = DV * E;               // pool bytes per V row
+    static constexpr int ROWB_M = DM * E;
+    static constexpr int TN0 = 16384 / ROWB_M;
     static constexpr int TN = TN0 > 128 ? 128 : TN0;    // tokens per tile (K+V <= 32 KB)
-    static constexpr int LCH = ROWB / 16;               // 16-byte chunks per row
-    static constexpr int RPI = 64 / LCH;                // rows per wave-wide copy
+    static constexpr int LCH_K = ROWB_K / 16;           // 16-byte chunks per K row
+    static constexpr int LCH_V = ROWB_V / 16;
+    static constexpr int RPI_K = 64 / LCH_K;            // K rows per wave-wide copy
+    static constexpr int RPI_V = 64 / LCH_V;
     static constexpr int NBUF = prefix_ring_stages(NQB);  // tiles in the LDS ring
-    static constexpr int STAGE_K = TN * ROWB;
-    static constexpr int STAGE = 2 * STAGE_K;           // K tile then V tile
-    static constexpr int NIKW = TN * LCH / (64 * NW);   // K copies per wave per tile (V: same)
-    static constexpr int RW = NIKW * RPI;               // rows each wave copies per tile
+    static constexpr int STAGE_K = TN * ROWB_M;         // K region; the V region follows
+    static constexpr int STAGE = 2 * STAGE_K;
+    static constexpr int NIKW_K = TN * LCH_K / (64 * NW);  // K copies per wave per tile
+    static constexpr int NIKW_V = TN * LCH_V / (64 * NW);  // V copies per wave per tile
+    static constexpr int NCP = NIKW_K + NIKW_V;
+    static constexpr int RW = TN / NW;                  // rows each wave copies per tile
     static constexpr int NIDX = 3;                      // index slots per wave
-    static_assert(NIKW >= 1 && NIKW * 64 * NW == TN * LCH, "tile / copy geometry");
+    static_assert(NIKW_K >= 1 && NIKW_K * 64 * NW == TN * LCH_K, "K tile / copy geometry");
+    static_assert(NIKW_V >= 1 && NIKW_V * 64 * NW == TN * LCH_V, "V tile / copy geometry");
+    static_assert(NIKW_K * RPI_K == RW && NIKW_V * RPI_V == RW, "K and V copies cover the same rows");
     static_assert(2 * RW <= 64, "one index copy per wave per tile");
-    static_assert(TN == tile_tokens_for(D, E), "host and kernel tile rules agree");
+    static_assert(TN == tile_tokens_for(D, DV, E), "host and kernel tile rules agree");
 };
 
 // LDS layouts (per ring stage; rows of raw pool bytes, 16-byte chunks; the
@@ -462,19 +474,21 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 // (the range lookup); they are preloaded into SGPRs at wave launch, so the
 // kv_indptr loads issue without waiting for the kernel-argument fetch.  The
 // same fields are also in p.
-template <bool FP8, int D, int NQB>
+template <bool FP8, int D, int DV, int NQB>
 __global__ __launch_bounds__(prefix_waves(NQB) * 64, 2) void prefix_kernel(
     const int32_t *kv_indptr, const int32_t *qo_indptr, const int64_t *kv_indices, int32_t bs, int32_t mode,
     int32_t split_tokens, int32_t total_tokens, int32_t h_kv, int32_t row_chunks, int32_t n_splits,
     const PrefixParams p)
 {
-    using G = PrefixGeom<FP8, D, NQB>;
+    using G = PrefixGeom<FP8, D, DV, NQB>;
     constexpr int NW = G::NW;
     constexpr int TN = G::TN;
-    constexpr int ROWB = G::ROWB;
-    constexpr int LCH = G::LCH;
+    constexpr int ROWB_K = G::ROWB_K;
+    constexpr int ROWB_V = G::ROWB_V;
+    constexpr int LCH_K = G::LCH_K;
+    constexpr int LCH_V = G::LCH_V;
     constexpr int NBUF = G::NBUF;
-    constexpr int NIKW = G::NIKW;
+    constexpr int NCP = G::NCP;
     constexpr int RW = G::RW;
     constexpr int NKS = D / 16;             // k-steps of the score MFMA
     constexpr int NSUB = TN / 32;           // 32-token sub-tiles per tile
@@ -484,22 +498,25 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64, 2) void prefix_kernel(
     // max / sum; the TS token shares are merged after the last tile.
     constexpr int TS = GW < NSUB ? GW : NSUB;
     constexpr int CS = GW / TS;
-    constexpr int DWV = D / CS;             // output columns per wave
+    constexpr int DWV = DV / CS;            // output columns per wave
     constexpr int DBW = DWV / 32;           // 32-column blocks per wave
     static_assert(TS * CS == GW && NSUB % TS == 0, "work split");
-    constexpr int KSWZ = (LCH < 16 ? LCH : 16) - 1;
-    constexpr int VSWZ_ROWS = LCH >= 16 ? 3 : 1;  // bf16: rows whose 4-chunk groups differ
-    constexpr int SW8_SHIFT = ROWB >= 256 ? 0 : (ROWB == 128 ? 1 : 2);  // fp8: log2(256 / row bytes)
-    auto kswz = [](int r) { return FP8 ? ((r >> SW8_SHIFT) & KSWZ) : (r & KSWZ); };
-    auto vswz = [](int r) { return FP8 ? ((r >> SW8_SHIFT) & KSWZ) : ((r & VSWZ_ROWS) << 2); };
+    constexpr int KSWZ = (LCH_K < 16 ? LCH_K : 16) - 1;
+    constexpr int VSWZ8 = (LCH_V < 16 ? LCH_V : 16) - 1;
+    constexpr int VSWZ_ROWS = LCH_V >= 16 ? 3 : 1;  // bf16: rows whose 4-chunk groups differ
+    // fp8: log2(256 / row bytes)
+    constexpr int SW8_SHIFT_K = ROWB_K >= 256 ? 0 : (ROWB_K == 128 ? 1 : 2);
+    constexpr int SW8_SHIFT_V = ROWB_V >= 256 ? 0 : (ROWB_V == 128 ? 1 : 2);
+    auto kswz = [](int r) { return FP8 ? ((r >> SW8_SHIFT_K) & KSWZ) : (r & KSWZ); };
+    auto vswz = [](int r) { return FP8 ? ((r >> SW8_SHIFT_V) & VSWZ8) : ((r & VSWZ_ROWS) << 2); };
     constexpr float kRescale = 8.0f;        // log2 headroom before the max is raised
     static_assert(NQB == 1 || NQB == 2, "query blocks");
     static_assert(NQB * 32 * D * 2 <= G::STAGE, "query tile fits one ring stage");
     static_assert(TN % 32 == 0 && DWV % 32 == 0, "tile / column geometry");
     // after tile t's copies, the next two steps issue 2 index copies and up to
-    // 2 * 2 * NIKW tile copies
-    constexpr int VM_TWO_AHEAD = 2 + 4 * NIKW;
-    constexpr int VM_ONE_AHEAD = 2 + 2 * NIKW;
+    // 2 * NCP tile copies
+    constexpr int VM_TWO_AHEAD = 2 + 2 * NCP;
+    constexpr int VM_ONE_AHEAD = 2 + NCP;
     constexpr int VM_NONE_AHEAD = 2;
 
     __shared__ __attribute__((aligned(1024))) uint8_t s_ring[NBUF * G::STAGE];
@@ -547,22 +564,41 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64, 2) void prefix_kernel(
     const uint8_t *vbase = p.v_buf + (int64_t)kvh * p.vb_s1;
     auto issue_tile = [&](int k) {
         const int64_t *ix = &s_idx[wave][k % G::NIDX][0];
-        const uint32_t st = ring + (k % NBUF) * G::STAGE + wave * NIKW * 1024;
-#pragma unroll
-        for (int i = 0; i < NIKW; ++i) {
-            const int rl = i * G::RPI + lane / LCH;   // row within this wave's rows
-            const int row = wave * RW + rl;           // row within the tile
-            const int pc = lane % LCH;                // LDS chunk within the row
-            const int vz = vswz(row);
-            const int tok = k * TN + row;
+        // this wave's rows wave*RW .. +RW sit at byte wave*RW*row_bytes of
+        // each region; one wave-wide copy moves 1 KB (RPI rows)
+        const uint32_t st = ring + (k % NBUF) * G::STAGE;
+        auto pool_row = [&](int rl) {
+            const int tok = k * TN + wave * RW + rl;
             uint64_t t = (uint64_t)ix[rl];
             if (paged)  // pool row = page id * page_size + position in the page
                 t = (uint64_t)(uint32_t)t * (uint32_t)p.page_size + (uint32_t)((pstart + tok) % p.page_size);
-            t = tok < len ? t : 0;
-            dma16(kbase + t * p.kb_s0 + ((pc ^ kswz(row)) << 4),
-                  __builtin_amdgcn_readfirstlane(st + i * 1024));
-            dma16(vbase + t * p.vb_s0 + ((pc ^ vz) << 4),
-                  __builtin_amdgcn_readfirstlane(st + G::STAGE_K + i * 1024));
+            return tok < len ? t : (uint64_t)0;
+        };
+        // every copy's pool row first: the copies are asm with a memory
+        // clobber, so an index read between them would be read again; K and V
+        // rows of equal size share their rows
+        constexpr bool SAME = LCH_K == LCH_V;
+        uint64_t tk[G::NIKW_K], tv[G::NIKW_V];
+#pragma unroll
+        for (int i = 0; i < G::NIKW_K; ++i)
+            tk[i] = pool_row(i * G::RPI_K + lane / LCH_K);
+#pragma unroll
+        for (int i = 0; i < G::NIKW_V; ++i)
+            tv[i] = SAME ? tk[i < G::NIKW_K ? i : 0] : pool_row(i * G::RPI_V + lane / LCH_V);
+#pragma unroll
+        for (int i = 0; i < (G::NIKW_K > G::NIKW_V ? G::NIKW_K : G::NIKW_V); ++i) {
+            if (i < G::NIKW_K) {
+                const int rl = i * G::RPI_K + lane / LCH_K;  // row within this wave's rows
+                const int pc = lane % LCH_K;                 // LDS chunk within the row
+                dma16(kbase + tk[i] * p.kb_s0 + ((pc ^ kswz(wave * RW + rl)) << 4),
+                      __builtin_amdgcn_readfirstlane(st + wave * RW * ROWB_K + i * 1024));
+            }
+            if (i < G::NIKW_V) {
+                const int rl = i * G::RPI_V + lane / LCH_V;
+                const int pc = lane % LCH_V;
+                dma16(vbase + tv[i] * p.vb_s0 + ((pc ^ vswz(wave * RW + rl)) << 4),
+                      __builtin_amdgcn_readfirstlane(st + G::STAGE_K + wave * RW * ROWB_V + i * 1024));
+            }
         }
     };
     // query tile -> ring stage NBUF-1: bf16 rows of D, chunk c of local row r
@@ -652,14 +688,14 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64, 2) void prefix_kernel(
     if (mode != 1 && kvh == 0 && rc == 0 && rg.start == 0 && tid == 0)
         ((i32x2_t *)p.seq_ranges)[rg.b] = i32x2_t{(int32_t)cidx, rg.seq_ranges};
     const int64_t slot = cidx * h_kv + kvh;
-    uint16_t *po = p.part_o + slot * (int64_t)rows * D;
+    uint16_t *po = p.part_o + slot * (int64_t)rows * DV;
     float *pl = p.part_lse + slot * (int64_t)rows;
     if (rg.start >= rg.end) {
         // Empty range (mode 1 past the end): output 0 and log-sum-exp -inf, so
         // the merge weight is exactly 0 and no stale value can leak in.
         const int nr = min(rows - row0, NQB * 32);
-        for (int e = tid; e < nr * D; e += NW * 64)
-            po[(int64_t)(row0 + e / D) * D + (e % D)] = 0;
+        for (int e = tid; e < nr * DV; e += NW * 64)
+            po[(int64_t)(row0 + e / DV) * DV + (e % DV)] = 0;
         if (tid < nr)
             pl[row0 + tid] = -INFINITY;
         return;
@@ -693,23 +729,23 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64, 2) void prefix_kernel(
     if constexpr (NBUF == 4) {
         issue_idx(3);
         if (1 < nt) {
-            wait_vm<QPW + 2 * NIKW + 2>();  // index slot 1: then slot 2, query, tile 0, slot 3
+            wait_vm<QPW + NCP + 2>();  // index slot 1: then slot 2, query, tile 0, slot 3
             issue_tile(1);
         }
         issue_idx(4);
         if (2 < nt) {
-            wait_vm<QPW + 4 * NIKW + 2>();  // index slot 2: then query, tile 0, slot 3, tile 1, slot 4
+            wait_vm<QPW + 2 * NCP + 2>();  // index slot 2: then query, tile 0, slot 3, tile 1, slot 4
             issue_tile(2);
         }
         // the query tile: then min(nt, 3) tiles and index slots 3, 4
         if (nt >= 3)
-            wait_vm<2 + 6 * NIKW>();
+            wait_vm<2 + 3 * NCP>();
         else if (nt == 2)
-            wait_vm<2 + 4 * NIKW>();
+            wait_vm<2 + 2 * NCP>();
         else
-            wait_vm<2 + 2 * NIKW>();
+            wait_vm<2 + NCP>();
     } else {
-        wait_vm<2 * NIKW>();  // the query tile: then tile 0
+        wait_vm<NCP>();  // the query tile: then tile 0
     }
     lds_barrier();
 
@@ -788,7 +824,7 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64, 2) void prefix_kernel(
             const int j = t + NBUF - 1;
             issue_idx(j + 2);
             if (j < nt) {
-                wait_vm<4 * NIKW + 2>();  // index slot j, copied two steps ago
+                wait_vm<2 * NCP + 2>();  // index slot j, copied two steps ago
                 issue_tile(j);
             }
         }
@@ -817,8 +853,8 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64, 2) void prefix_kernel(
                 if constexpr (FP8) {
                     // d = 64 ks + 32 half + 0..31: chunks 4 ks + 2 half, +1
                     const int c0 = 4 * ks + 2 * half;
-                    const u32x4_t lo = *(const u32x4_t *)(K + krow * ROWB + ((c0 ^ kswz(krow)) << 4));
-                    const u32x4_t hi = *(const u32x4_t *)(K + krow * ROWB + (((c0 + 1) ^ kswz(krow)) << 4));
+                    const u32x4_t lo = *(const u32x4_t *)(K + krow * ROWB_K + ((c0 ^ kswz(krow)) << 4));
+                    const u32x4_t hi = *(const u32x4_t *)(K + krow * ROWB_K + (((c0 + 1) ^ kswz(krow)) << 4));
                     const i32x8_t a = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                                        (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
                     if (ks & 1)
@@ -827,7 +863,7 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64, 2) void prefix_kernel(
                         sc = mfma32x32x64_fp8(a, qreg[ks], sc);
                 } else {
                     const int ch = (ks * 2 + half) ^ kswz(krow);
-                    const bf16x8_t a = as_bf16x8(*(const u32x4_t *)(K + krow * ROWB + (ch << 4)));
+                    const bf16x8_t a = as_bf16x8(*(const u32x4_t *)(K + krow * ROWB_K + (ch << 4)));
                     if (ks & 1)
                         sc2 = mfma32x32x16(a, qreg[ks], sc2);
                     else
@@ -897,7 +933,7 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64, 2) void prefix_kernel(
                             const int tok = sub * 32 + kh * 16 + 4 * half + (t8 < 4 ? t8 : t8 + 4);
                             const int pc = (col >> 4) ^ vswz(tok);
                             const i32x2_t raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                                (__attribute__((address_space(3))) i32x2_t *)(V + tok * ROWB + (pc << 4) + (col & 15)));
+                                (__attribute__((address_space(3))) i32x2_t *)(V + tok * ROWB_V + (pc << 4) + (col & 15)));
                             // E4M3FN -> bf16 is exact; the hardware conversion
                             // decodes the OCP format
                             a = u32x4_t{cvt_e4m3x2_bf16<false>(raw[0]), cvt_e4m3x2_bf16<true>(raw[0]),
@@ -912,7 +948,7 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64, 2) void prefix_kernel(
                             for (int r = 0; r < 2; ++r) {
                                 const int tok = sub * 32 + kh * 16 + 8 * r + 4 * half + (g16 >> 2);
                                 const int pc = (col >> 3) ^ vswz(tok);
-                                const uint8_t *src = V + tok * ROWB + (pc << 4) + (col & 7) * 2;
+                                const uint8_t *src = V + tok * ROWB_V + (pc << 4) + (col & 7) * 2;
                                 const i16x4_t v4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                                     (__attribute__((address_space(3))) i16x4_t *)(src));
                                 const u32x2_t w2 = __builtin_bit_cast(u32x2_t, v4);
@@ -1037,7 +1073,7 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64, 2) void prefix_kernel(
                 const int dv = cs * DWV + db * 32 + 8 * g4 + 4 * half;
                 const u32x2_t o = {pack_bf16x2(oacc[db][4 * g4] * inv, oacc[db][4 * g4 + 1] * inv),
                                    pack_bf16x2(oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv)};
-                *(u32x2_t *)(po + (int64_t)r * D + dv) = o;
+                *(u32x2_t *)(po + (int64_t)r * DV + dv) = o;
             }
         }
         if (ts == 0 && cs == 0 && half == 0)
@@ -1077,12 +1113,13 @@ __device__ __forceinline__ void load_bf16_row(const uint16_t *src, float (&dst)[
 // batch is issued, and lanes past the sequence's ranges or draft rows re-read
 // a valid row, so depths beyond what the batch needs only move duplicate
 // bytes (a decode step has one or two ranges and one draft row per sequence).
-template <int D, int PRE, int PRE_D>
+template <int D, int DV, int PRE, int PRE_D>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     const int32_t *kv_indptr, const int32_t *qo_indptr, int32_t bs, int32_t mode, int32_t split_tokens,
     int32_t n_splits, int32_t h_kv, int32_t rows, const CombineParams p)
 {  // leading arguments preloaded into SGPRs, as for the prefix kernel
-    constexpr int VPL = D / 64;  // elements of D / Dv per lane
+    constexpr int VPL = D / 64;    // elements of a query / key row per lane
+    constexpr int VPLV = DV / 64;  // elements of a value / output row per lane
     static_assert(PRE >= 1 && PRE <= 64 && PRE_D >= 1 && PRE_D <= 64, "preload depths");
 
     const int lane = threadIdx.x & 63;
@@ -1097,7 +1134,8 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     const int hg = r / p.l_ext;
     const int di = r % p.l_ext;
     const int h = kvh * p.group + hg;
-    const int d0 = lane * VPL;
+    const int d0 = lane * VPL;    // this lane's query / key elements
+    const int dv0 = lane * VPLV;  // this lane's value / output elements
 
     // ---- first load round: where this sequence's rows and ranges are ----
     const int qo = qo_indptr[b];
@@ -1118,19 +1156,21 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     // ---- second load round: log-sum-exps, partial outputs, query row, draft rows ----
     const int64_t lse_step = (int64_t)p.h_kv * p.rows;  // next range, same head and row
     const float *lse_row = p.part_lse + ((int64_t)base * p.h_kv + kvh) * p.rows + r;
-    const uint16_t *o_row = p.part_o + (((int64_t)base * p.h_kv + kvh) * p.rows + r) * D + d0;
-    const int64_t o_step = lse_step * D;
+    const uint16_t *o_row = p.part_o + (((int64_t)base * p.h_kv + kvh) * p.rows + r) * DV + dv0;
+    const int64_t o_step = lse_step * DV;
     // Every load below is unconditional: a lane or slot past the sequence's
-    // ranges re-reads a valid address (the query row, or the last range) and
-    // gets weight 0, so the compiler issues all loads before the first wait.
+    // ranges re-reads a valid address (the query row, the sequence's first
+    // draft value row, or the last range) and gets weight 0, so the compiler
+    // issues all loads before the first wait.
     const uint16_t *q_row = p.q + (int64_t)(qo + di) * p.q_s0 + (int64_t)h * p.q_s1;
+    const uint16_t *v_row0 = p.v_ext + (int64_t)qo * p.ve_s0 + (int64_t)kvh * p.ve_s1 + dv0;
     const int last = count > 0 ? count - 1 : 0;
     float lse0 = *(lane < count ? lse_row + lane * lse_step : (const float *)q_row);  // range s = lane
     lse0 = lane < count ? lse0 : -INFINITY;
-    float ov[PRE][VPL];
+    float ov[PRE][VPLV];
 #pragma unroll
     for (int i = 0; i < PRE; ++i)
-        load_bf16_row<VPL>(count > 0 ? o_row + (i < count ? i : last) * o_step : q_row + d0, ov[i]);
+        load_bf16_row<VPLV>(count > 0 ? o_row + (i < count ? i : last) * o_step : v_row0, ov[i]);
     float qv[VPL];
     load_bf16_row<VPL>(q_row + d0, qv);
     // visible draft keys j < 64 as bits: mask bytes (one lane per key) or j <= di
@@ -1141,12 +1181,12 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     } else {
         vis = di >= 63 ? ~0ull : ((2ull << di) - 1);
     }
-    float kd[PRE_D][VPL], vd[PRE_D][VPL];
+    float kd[PRE_D][VPL], vd[PRE_D][VPLV];
 #pragma unroll
     for (int j = 0; j < PRE_D; ++j) {
         const int jj = j < L ? j : 0;  // rows past the sequence's drafts are loaded but unused
         load_bf16_row<VPL>(p.k_ext + (int64_t)(qo + jj) * p.ke_s0 + (int64_t)kvh * p.ke_s1 + d0, kd[j]);
-        load_bf16_row<VPL>(p.v_ext + (int64_t)(qo + jj) * p.ve_s0 + (int64_t)kvh * p.ve_s1 + d0, vd[j]);
+        load_bf16_row<VPLV>(p.v_ext + (int64_t)(qo + jj) * p.ve_s0 + (int64_t)kvh * p.ve_s1 + dv0, vd[j]);
     }
 
     // ---- (a) prefix ranges ----
@@ -1155,9 +1195,9 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
         m = fmaxf(m, lse_row[s * lse_step]);
     m = wave_max(m);
     float den = 0.0f;
-    float acc[VPL];
+    float acc[VPLV];
 #pragma unroll
-    for (int v = 0; v < VPL; ++v)
+    for (int v = 0; v < VPLV; ++v)
         acc[v] = 0.0f;
     if (m > -INFINITY) {  // an empty range (lse -inf) has weight 0 and output 0
         float e = lane < count ? __expf(lse0 - m) : 0.0f;
@@ -1177,13 +1217,13 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
                 }
 #pragma unroll
                 for (int i = 0; i < PRE; ++i)
-                    load_bf16_row<VPL>(o_row + (s0 + i < count ? s0 + i : last) * o_step, ov[i]);
+                    load_bf16_row<VPLV>(o_row + (s0 + i < count ? s0 + i : last) * o_step, ov[i]);
             }
 #pragma unroll
             for (int i = 0; i < PRE; ++i) {
                 const float w = lane_f(w_c, (s0 & 63) + i);
 #pragma unroll
-                for (int v = 0; v < VPL; ++v)
+                for (int v = 0; v < VPLV; ++v)
                     acc[v] += w * ov[i][v];
             }
         }
@@ -1210,9 +1250,9 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
             md = fmaxf(md, sj[j]);
     }
     float dd = 0.0f;
-    float od[VPL];
+    float od[VPLV];
 #pragma unroll
-    for (int v = 0; v < VPL; ++v)
+    for (int v = 0; v < VPLV; ++v)
         od[v] = 0.0f;
 #pragma unroll
     for (int j = 0; j < PRE_D; ++j) {
@@ -1220,7 +1260,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
             const float w = __expf(sj[j] - md);
             dd += w;
 #pragma unroll
-            for (int v = 0; v < VPL; ++v)
+            for (int v = 0; v < VPLV; ++v)
                 od[v] += w * vd[j][v];
         }
     }
@@ -1229,9 +1269,9 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     for (int j = PRE_D; j < jend; ++j) {
         if (p.mask && !((vis >> j) & 1))
             continue;
-        float kj[VPL], vj[VPL];
+        float kj[VPL], vj[VPLV];
         load_bf16_row<VPL>(p.k_ext + (int64_t)(qo + j) * p.ke_s0 + (int64_t)kvh * p.ke_s1 + d0, kj);
-        load_bf16_row<VPL>(p.v_ext + (int64_t)(qo + j) * p.ve_s0 + (int64_t)kvh * p.ve_s1 + d0, vj);
+        load_bf16_row<VPLV>(p.v_ext + (int64_t)(qo + j) * p.ve_s0 + (int64_t)kvh * p.ve_s1 + dv0, vj);
         float dot = 0.0f;
 #pragma unroll
         for (int v = 0; v < VPL; ++v)
@@ -1241,7 +1281,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
         const float a = __expf(md - mn);
         const float w = __expf(s - mn);
 #pragma unroll
-        for (int v = 0; v < VPL; ++v)
+        for (int v = 0; v < VPLV; ++v)
             od[v] = od[v] * a + w * vj[v];
         dd = dd * a + w;
         md = mn;
@@ -1255,82 +1295,95 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     const float wd = dd > 0.0f ? __expf(md - mm) : 0.0f;
     const float tot = wp * den + wd * dd;
     const float inv = tot > 0.0f ? 1.0f / tot : 0.0f;
-    uint16_t *orow = p.out + (int64_t)(qo + di) * p.o_s0 + (int64_t)h * p.o_s1 + d0;
-    uint32_t ob[VPL];
+    uint16_t *orow = p.out + (int64_t)(qo + di) * p.o_s0 + (int64_t)h * p.o_s1 + dv0;
+    uint32_t ob[VPLV];
 #pragma unroll
-    for (int v = 0; v < VPL; ++v)
+    for (int v = 0; v < VPLV; ++v)
         ob[v] = f32_to_bf16_rne((wp * acc[v] + wd * od[v]) * inv);
-    if constexpr (VPL == 4)
+    if constexpr (VPLV == 4)
         *(u32x2_t *)orow = u32x2_t{ob[0] | (ob[1] << 16), ob[2] | (ob[3] << 16)};
-    else if constexpr (VPL == 2)
+    else if constexpr (VPLV == 2)
         *(uint32_t *)orow = ob[0] | (ob[1] << 16);
     else
         orow[0] = (uint16_t)ob[0];
 }
 
 // ----------------------------------------------------------------- launch ---
-template <bool FP8, int D>
+template <bool FP8, int D, int DV>
 static int launch_prefix_qb(const PrefixParams &p, int qblocks, int64_t blocks, hipStream_t s)
 {
     dim3 grid((unsigned)blocks), block(prefix_waves(qblocks) * 64);
 #define VA_PREFIX_ARGS p.kv_indptr, p.qo_indptr, p.kv_indices, p.bs, p.mode, p.split_tokens, p.total_tokens, \
                        p.h_kv, p.row_chunks, p.n_splits, p
     if (qblocks == 1)
-        hipLaunchKernelGGL((prefix_kernel<FP8, D, 1>), grid, block, 0, s, VA_PREFIX_ARGS);
+        hipLaunchKernelGGL((prefix_kernel<FP8, D, DV, 1>), grid, block, 0, s, VA_PREFIX_ARGS);
     else
-        hipLaunchKernelGGL((prefix_kernel<FP8, D, 2>), grid, block, 0, s, VA_PREFIX_ARGS);
+        hipLaunchKernelGGL((prefix_kernel<FP8, D, DV, 2>), grid, block, 0, s, VA_PREFIX_ARGS);
 #undef VA_PREFIX_ARGS
     return (int)hipGetLastError();
 }
 
-int launch_prefix(const PrefixParams &p, int head_dim, bool kv_fp8, int qblocks, int64_t blocks,
-                  void *stream)
+template <bool FP8>
+static int launch_prefix_dims(const PrefixParams &p, int head_dim, int v_head_dim, int qblocks, int64_t blocks,
+                              hipStream_t s)
 {
-    hipStream_t s = (hipStream_t)stream;
-    if (kv_fp8) {
-        switch (head_dim) {
-        case 64: return launch_prefix_qb<true, 64>(p, qblocks, blocks, s);
-        case 128: return launch_prefix_qb<true, 128>(p, qblocks, blocks, s);
-        default: return launch_prefix_qb<true, 256>(p, qblocks, blocks, s);
-        }
-    }
-    switch (head_dim) {
-    case 64: return launch_prefix_qb<false, 64>(p, qblocks, blocks, s);
-    case 128: return launch_prefix_qb<false, 128>(p, qblocks, blocks, s);
-    default: return launch_prefix_qb<false, 256>(p, qblocks, blocks, s);
+    // (head_dim, v_head_dim): equal, or one twice the other (the host checks)
+    switch (head_dim * 1000 + v_head_dim) {
+    case 64064: return launch_prefix_qb<FP8, 64, 64>(p, qblocks, blocks, s);
+    case 64128: return launch_prefix_qb<FP8, 64, 128>(p, qblocks, blocks, s);
+    case 128064: return launch_prefix_qb<FP8, 128, 64>(p, qblocks, blocks, s);
+    case 128128: return launch_prefix_qb<FP8, 128, 128>(p, qblocks, blocks, s);
+    case 128256: return launch_prefix_qb<FP8, 128, 256>(p, qblocks, blocks, s);
+    case 256128: return launch_prefix_qb<FP8, 256, 128>(p, qblocks, blocks, s);
+    case 256256: return launch_prefix_qb<FP8, 256, 256>(p, qblocks, blocks, s);
+    default: return (int)hipErrorInvalidValue;
     }
 }
 
-template <int D, int PRE>
+int launch_prefix(const PrefixParams &p, int head_dim, int v_head_dim, bool kv_fp8, int qblocks, int64_t blocks,
+                  void *stream)
+{
+    hipStream_t s = (hipStream_t)stream;
+    return kv_fp8 ? launch_prefix_dims<true>(p, head_dim, v_head_dim, qblocks, blocks, s)
+                  : launch_prefix_dims<false>(p, head_dim, v_head_dim, qblocks, blocks, s);
+}
+
+template <int D, int DV, int PRE>
 static void launch_combine_d(const CombineParams &p, int pre_d, dim3 grid, dim3 block, hipStream_t s)
 {
 #define VA_COMBINE_ARGS p.kv_indptr, p.qo_indptr, p.bs, p.mode, p.split_tokens, p.n_splits, p.h_kv, p.rows, p
     if (pre_d == 1)
-        hipLaunchKernelGGL((combine_kernel<D, PRE, 1>), grid, block, 0, s, VA_COMBINE_ARGS);
+        hipLaunchKernelGGL((combine_kernel<D, DV, PRE, 1>), grid, block, 0, s, VA_COMBINE_ARGS);
     else if (pre_d == 4)
-        hipLaunchKernelGGL((combine_kernel<D, PRE, 4>), grid, block, 0, s, VA_COMBINE_ARGS);
+        hipLaunchKernelGGL((combine_kernel<D, DV, PRE, 4>), grid, block, 0, s, VA_COMBINE_ARGS);
     else
-        hipLaunchKernelGGL((combine_kernel<D, PRE, 8>), grid, block, 0, s, VA_COMBINE_ARGS);
+        hipLaunchKernelGGL((combine_kernel<D, DV, PRE, 8>), grid, block, 0, s, VA_COMBINE_ARGS);
 #undef VA_COMBINE_ARGS
 }
 
-template <int D>
+template <int D, int DV>
 static void launch_combine_pre(const CombineParams &p, int pre, int pre_d, dim3 grid, dim3 block, hipStream_t s)
 {
     if (pre == 8)
-        launch_combine_d<D, 8>(p, pre_d, grid, block, s);
+        launch_combine_d<D, DV, 8>(p, pre_d, grid, block, s);
     else
-        launch_combine_d<D, 32>(p, pre_d, grid, block, s);
+        launch_combine_d<D, DV, 32>(p, pre_d, grid, block, s);
 }
 
-int launch_combine(const CombineParams &p, int head_dim, int pre, int pre_d, int64_t blocks, void *stream)
+int launch_combine(const CombineParams &p, int head_dim, int v_head_dim, int pre, int pre_d, int64_t blocks,
+                   void *stream)
 {
     hipStream_t s = (hipStream_t)stream;
     dim3 grid((unsigned)blocks), block(kCombineThreads);
-    switch (head_dim) {
-    case 64: launch_combine_pre<64>(p, pre, pre_d, grid, block, s); break;
-    case 128: launch_combine_pre<128>(p, pre, pre_d, grid, block, s); break;
-    default: launch_combine_pre<256>(p, pre, pre_d, grid, block, s); break;
+    switch (head_dim * 1000 + v_head_dim) {
+    case 64064: launch_combine_pre<64, 64>(p, pre, pre_d, grid, block, s); break;
+    case 64128: launch_combine_pre<64, 128>(p, pre, pre_d, grid, block, s); break;
+    case 128064: launch_combine_pre<128, 64>(p, pre, pre_d, grid, block, s); break;
+    case 128128: launch_combine_pre<128, 128>(p, pre, pre_d, grid, block, s); break;
+    case 128256: launch_combine_pre<128, 256>(p, pre, pre_d, grid, block, s); break;
+    case 256128: launch_combine_pre<256, 128>(p, pre, pre_d, grid, block, s); break;
+    case 256256: launch_combine_pre<256, 256>(p, pre, pre_d, grid, block, s); break;
+    default: return (int)hipErrorInvalidValue;
     }
     return (int)hipGetLastError();
 }

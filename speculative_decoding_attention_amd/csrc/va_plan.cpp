@@ -24,8 +24,6 @@ thread_local char g_last_error[512] = {0};
 
 int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
-bool supported_dim(int d) { return d == 64 || d == 128 || d == 256; }
-
 int fail(int code, const char *fmt, ...)
 {
     va_list ap;
@@ -64,8 +62,9 @@ int check_desc(const va_desc_t *d, int32_t l_ext)
     if (d->h_q < 1 || d->h_kv < 1 || d->h_q % d->h_kv != 0)
         return fail(VA_ERR_HEADS, "h_q = %d, h_kv = %d; need h_q a positive multiple of h_kv",
                     d->h_q, d->h_kv);
-    if (!supported_dim(d->head_dim) || d->v_head_dim != d->head_dim)
-        return fail(VA_ERR_HEAD_DIM, "head_dim = %d, v_head_dim = %d; supported: equal and in {64,128,256}",
+    if (!supported_head_dims(d->head_dim, d->v_head_dim))
+        return fail(VA_ERR_HEAD_DIM,
+                    "head_dim = %d, v_head_dim = %d; supported: both in {64,128,256}, equal or one twice the other",
                     d->head_dim, d->v_head_dim);
     if (d->kv_dtype != VA_DTYPE_BF16 && d->kv_dtype != VA_DTYPE_FP8_E4M3FN)
         return fail(VA_ERR_DTYPE, "kv_dtype = %d is not a va_dtype_t", d->kv_dtype);
@@ -150,7 +149,7 @@ int make_plan(const va_desc_t *d, int32_t l_ext, int32_t num_cus, va_plan_t *pla
         return fail(VA_ERR_SIZE, "rows per KV head (%lld) too large", (long long)rows);
     p.rows = (int32_t)rows;
     p.row_chunks = (int32_t)((rows + kRowChunk - 1) / kRowChunk);
-    p.tile_tokens = tile_tokens_for(d->head_dim, d->kv_dtype == VA_DTYPE_FP8_E4M3FN ? 1 : 2);
+    p.tile_tokens = tile_tokens_for(d->head_dim, d->v_head_dim, d->kv_dtype == VA_DTYPE_FP8_E4M3FN ? 1 : 2);
     const int64_t T = d->num_kv_indices;
     int64_t ranges;  // prefix workgroups per (KV head, row chunk)
     if (d->n_splits > 0) {
@@ -240,7 +239,7 @@ VA_API const char *verify_attn_strerror(int code)
     case VA_ERR_NULL_ARG: return "required pointer is NULL";
     case VA_ERR_BATCH: return "batch size must be >= 1";
     case VA_ERR_HEADS: return "h_q must be a positive multiple of h_kv";
-    case VA_ERR_HEAD_DIM: return "unsupported head dims (need equal, in {64,128,256})";
+    case VA_ERR_HEAD_DIM: return "unsupported head dims (need both in {64,128,256}, equal or one twice the other)";
     case VA_ERR_DTYPE: return "unsupported pool dtype";
     case VA_ERR_EXTEND: return "l_ext < 1 or q_rows != bs * l_ext";
     case VA_ERR_STRIDE: return "invalid stride";

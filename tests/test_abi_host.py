@@ -62,7 +62,8 @@ def test_valid_descriptor_passes():
     (lambda d: setattr(d, "h_kv", 3), 4, -3),          # 16 % 3 != 0
     (lambda d: setattr(d, "h_kv", 0), 4, -3),
     (lambda d: setattr(d, "head_dim", 96), 4, -4),
-    (lambda d: setattr(d, "v_head_dim", 128), 4, -4),  # D != Dv
+    (lambda d: setattr(d, "v_head_dim", 64), 4, -4),   # Dv = D / 4
+    (lambda d: setattr(d, "v_head_dim", 96), 4, -4),
     (lambda d: setattr(d, "kv_dtype", 7), 4, -5),
     (lambda d: None, 0, -6),                            # l_ext < 1
     (lambda d: None, 5, -6),                            # ragged: q_rows != bs * (mle + 1)
@@ -79,6 +80,23 @@ def test_invalid_descriptors_are_rejected(mutate, l_ext, code):
     assert va.verify_attn_check(d, l_ext) == code
     assert va.lib().verify_attn_last_error().decode() != ""
     assert va.lib().verify_attn_strerror(code).decode() not in ("", "unknown status")
+
+
+@pytest.mark.parametrize("d,dv,ok", [(64, 128, True), (128, 64, True), (128, 256, True), (256, 128, True),
+                                     (64, 256, False), (256, 64, False), (256, 96, False)])
+def test_value_head_dim_pairs(d, dv, ok):
+    # head_dim and v_head_dim are separate (the pages' VerifySplitKV takes
+    # both); the kernels are built for equal dims and dims a factor 2 apart
+    meta = meta_problem(d=d)
+    meta["v_ext"] = torch.empty(12, 2, dv, dtype=torch.bfloat16, device="meta")
+    meta["v_buf"] = torch.empty(3 * 512, 2, dv, dtype=torch.bfloat16, device="meta")
+    meta["out"] = torch.empty(12, 16, dv, dtype=torch.bfloat16, device="meta")
+    desc = va.make_desc(**meta)
+    assert (va.verify_attn_check(desc, 4) == 0) == ok
+    if ok:
+        plan = va.verify_attn_plan(desc, 4, 256)
+        assert plan.partial_bytes >= plan.range_slots * 2 * 32 * dv * 2
+        assert plan.tile_tokens == 16384 // (2 * max(d, dv))
 
 
 def test_null_descriptor():

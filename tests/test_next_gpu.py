@@ -86,13 +86,14 @@ def test_tree_headline_shape(va):
 
 
 # -------------------------------------------------------------------- append ---
-def append_case(kv_dtype, n, h_kv, d, pool, seed, scale_k=0.03125, scale_v=0.0625):
+def append_case(kv_dtype, n, h_kv, d, pool, seed, scale_k=0.03125, scale_v=0.0625, dv=None):
+    dv = d if dv is None else dv
     g = torch.Generator().manual_seed(seed)
     k = (torch.randn(n, h_kv, d, generator=g) * 3).to(torch.bfloat16)
-    v = (torch.randn(n, h_kv, d, generator=g) * 3).to(torch.bfloat16)
+    v = (torch.randn(n, h_kv, dv, generator=g) * 3).to(torch.bfloat16)
     loc = torch.randperm(pool, generator=g)[:n].to(torch.int64)
     kb = torch.randn(pool, h_kv, d, generator=g).to(kv_dtype)
-    vb = torch.randn(pool, h_kv, d, generator=g).to(kv_dtype)
+    vb = torch.randn(pool, h_kv, dv, generator=g).to(kv_dtype)
     return k, v, loc, kb, vb, scale_k, scale_v
 
 
@@ -113,6 +114,18 @@ def test_append_bit_exact(va, kv_dtype, d):
     kg, vg, lg = k.to(dev()), v.to(dev()), loc.to(dev())
     kbg, vbg = kb.to(dev()), vb.to(dev())
     va.verify_attn_append_kv(kg, vg, lg, kbg, vbg, ks, vs)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(kbg), ek)
+    np.testing.assert_array_equal(bits(vbg), ev)
+
+
+@pytest.mark.parametrize("d,dv", [(64, 128), (128, 64), (128, 256), (256, 128)])
+@pytest.mark.parametrize("kv_dtype", [torch.bfloat16, torch.float8_e4m3fn])
+def test_append_value_head_dim_differs(va, kv_dtype, d, dv):
+    k, v, loc, kb, vb, ks, vs = append_case(kv_dtype, 300, 2, d, 1000, seed=d + dv, dv=dv)
+    ek, ev = oracle.append_kv(k, v, loc, kb, vb, ks, vs)
+    kbg, vbg = kb.to(dev()), vb.to(dev())
+    va.verify_attn_append_kv(k.to(dev()), v.to(dev()), loc.to(dev()), kbg, vbg, ks, vs)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(bits(kbg), ek)
     np.testing.assert_array_equal(bits(vbg), ev)

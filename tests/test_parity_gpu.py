@@ -230,6 +230,29 @@ def test_every_prefix_kernel_shape(va, kv, d, rows):
     check_full(va, p)
 
 
+@pytest.mark.parametrize("rows", [16, 64])
+@pytest.mark.parametrize("d,dv", [(64, 128), (128, 64), (128, 256), (256, 128)])
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_value_head_dim_differs(va, kv, d, dv, rows):
+    # the pages keep head_dim and v_head_dim apart (verify_splitkv.py,
+    # _verify_prefix_stage1 BLOCK_DV; VerifySplitKV(..., head_dim,
+    # v_head_dim, ...)): scores over D, values / output over Dv, for every
+    # pair the kernels are built for and both prefix kernel shapes
+    hq, hkv, l_ext = (8, 2, 4) if rows == 16 else (8, 1, 8)
+    dt = torch.float8_e4m3fn if kv == "fp8" else torch.bfloat16
+    p = W.make_problem([300, 1000, 77, 0], l_ext, hq, hkv, d, dv, kv_dtype=dt, k_scale=0.5, v_scale=0.25,
+                       pool_factor=2, permute=True, seed=59, name="%s d%d dv%d rows %d" % (kv, d, dv, rows))
+    check_full(va, p)
+
+
+def test_value_head_dim_differs_long_and_split(va):
+    # D=256 / Dv=128 at 2 x 8k with k/v scales, heuristic and explicit splits
+    p = W.make_problem([8192, 5000], 4, 16, 2, 256, 128, k_scale=0.5, v_scale=0.25, pool_factor=2,
+                       permute=True, seed=60, name="d256 dv128 long")
+    check_full(va, p)
+    check_full(va, p, n_splits=16)
+
+
 def test_many_rows_two_row_chunks(va):
     # G=16, l_ext=8: 128 query rows per KV head -> two 64-row chunks
     check_full(va, W.make_problem([700, 1500], 8, 16, 1, 128, seed=57, name="128 rows"))
