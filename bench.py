@@ -216,7 +216,7 @@ def time_workload(torch, va, W, name, steps, warmup, replicas, seed0=1000, capac
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / (launches * steps_per_graph), host_us
 
-    ms_graph = ms_graph20 = ms_graph_cap = None
+    ms_graph = ms_graph20 = ms_graph_cap = ms_graph_cap20 = None
     host_graph_us = host_graph20_us = None
     try:
         ms_graph, host_graph_us = graph_loop(capture(runners, 1), 1)
@@ -233,6 +233,7 @@ def time_workload(torch, va, W, name, steps, warmup, replicas, seed0=1000, capac
             need = max(va.verify_attn_workspace_bytes(r.desc, r.p.l_ext) for r in caps)
             assert need <= ws.numel(), "capacity plan needs a larger workspace"
             ms_graph_cap, _ = graph_loop(capture(caps, 1), 1)
+            ms_graph_cap20, _ = graph_loop(capture(caps, 20), 20)
     except Exception as exc:  # report, never hide
         print("graph replay timing failed: %r" % (exc,), file=sys.stderr)
 
@@ -253,6 +254,7 @@ def time_workload(torch, va, W, name, steps, warmup, replicas, seed0=1000, capac
         us_step_graph20=us(ms_graph20) if ms_graph20 else None,
         host_us_per_graph20_launch=round(host_graph20_us, 2) if host_graph20_us else None,
         us_step_graph_capacity=us(ms_graph_cap) if ms_graph_cap else None,
+        us_step_graph_capacity20=us(ms_graph_cap20) if ms_graph_cap20 else None,
         capacity_factor=capacity_factor or None,
     )
 
@@ -536,7 +538,9 @@ def main():
                              "host_us_per_launch": head["host_us_per_graph_launch"],
                              "twenty_steps_per_graph_us_per_call": head["us_step_graph20"],
                              "host_us_per_twenty_step_launch": head["host_us_per_graph20_launch"],
-                             "kv_indices_capacity_4x_us_per_call": head["us_step_graph_capacity"]},
+                             "kv_indices_capacity_4x_us_per_call": head["us_step_graph_capacity"],
+                             "kv_indices_capacity_4x_twenty_steps_per_graph_us_per_call":
+                                 head["us_step_graph_capacity20"]},
             "secondary": secondary,
             "around_verify": extensions,
         },
