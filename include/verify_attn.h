@@ -83,9 +83,12 @@ typedef enum {
  * lie in [0, num_kv_indices].
  * Splitting (both 0 = the library's heuristic: the grid holds one range per
  * resident prefix workgroup, at least one per sequence and at most
- * ceil(num_kv_indices / 64), and the kernels pick the range size from
- * kv_indptr on every launch -- the smallest multiple of 64 tokens whose
- * ranges fit that grid -- so the split follows the lengths actually passed):
+ * ceil(num_kv_indices / 64) -- for a batch with more sequences than that,
+ * about one range per MiB of K/V per KV head -- and the kernels pick the
+ * range size from kv_indptr on every launch: the smallest multiple of 64
+ * tokens whose ranges fit that grid, or whole sequences for a batch past
+ * the resident workgroups whose prefixes are within 1/8 of equal; so the
+ * split follows the lengths actually passed):
  *   split_tokens > 0 : every prefix is cut into ranges of split_tokens tokens
  *                      (a multiple of 64), one work item each;
  *   n_splits > 0     : the pages' rule -- every prefix is cut into n_splits
@@ -116,7 +119,8 @@ typedef struct {
  * workspace sized once stays valid, as graph capture needs). */
 typedef struct {
     int32_t mode;            /* 0: heuristic (range size fitted on the device); 1: n_splits equal
-                                ranges per sequence; 2: ranges of split_tokens tokens */
+                                ranges per sequence; 2: ranges of split_tokens tokens; 3: the
+                                heuristic for a batch past the resident workgroups (rounds) */
     int32_t split_tokens;    /* mode 2: tokens per range; mode 0: the size num_kv_indices tokens in
                                 equal prefixes would get (where the kernels guess each range starts) */
     int32_t n_splits;        /* ranges per sequence (mode 1) */

@@ -31,6 +31,10 @@ constexpr int prefix_resident_per_cu(int qblocks) { return qblocks == 1 ? 2 : 1;
 constexpr int kMaxTreeDrafts = 64;
 // Smallest range the heuristic chooses; ranges are multiples of this.
 constexpr int kSplitQuantum = 64;
+// When a batch has more sequences than the CUs hold prefix workgroups, ranges
+// of about this many K/V bytes per KV head let the dispatcher balance the
+// rounds of workgroups (1024 tokens at bf16 D = Dv = 256).
+constexpr int64_t kRoundRangeBytes = int64_t(1) << 20;
 // Size of the library-owned device array verify_attn_run_noalloc keeps its
 // partials in (va_noalloc.hip): the headline and 64k-prefix workloads need
 // 8.5 MB of it on MI355X.

@@ -158,6 +158,10 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t 
 //     + n_splits - 1 of ceil(ceil(n_b / n_splits) / 32) * 32 tokens, empty
 //     past the end.
 //   mode 2 (explicit): as mode 0 with c = split_tokens.
+//   mode 3 (fitted, in rounds): mode 0 for a batch with more sequences than
+//     the CUs hold prefix workgroups; the grid allows ranges of about 1 MiB of
+//     K/V per KV head, and a batch of (nearly) equal prefixes keeps one range
+//     per sequence.
 struct Range {
     int32_t b;
     int32_t start;    // token range [start, end) of sequence b's prefix
@@ -228,11 +232,14 @@ __device__ __forceinline__ uint32_t batch_ranges(const int32_t *kv_indptr, const
 // least M / k and at most M / k + bs, so the answer lies in
 // [ceil(M / cap), ceil(M / (cap - bs))] (when cap > bs) and never above
 // max m_b; a binary search over whole-batch counts takes it from there.
+// `count` receives the number of ranges when it is known on the way (else
+// cap, an upper bound).
 template <int NC>
 __device__ __forceinline__ uint32_t fitted_range_units(const int32_t *kv_indptr, const int32_t *qo_indptr,
-                                                       int32_t bs, int32_t cap, const SeqGroup<NC> &first)
+                                                       int32_t bs, int32_t cap, bool rounds,
+                                                       const SeqGroup<NC> &first, uint32_t &count)
 {
-    uint32_t ms = 0, mx = 0;
+    uint32_t ms = 0, mx = 0, nz = 0;
     for (int32_t b0 = 0; b0 < bs; b0 += 64 * NC) {
         const SeqGroup<NC> g = b0 == 0 ? first : load_group<NC>(kv_indptr, qo_indptr, bs, b0);
 #pragma unroll
@@ -240,36 +247,60 @@ __device__ __forceinline__ uint32_t fitted_range_units(const int32_t *kv_indptr,
             const uint32_t m = (seq_len(g, c, b0, bs) + 63u) >> 6;
             ms += m;
             mx = max(mx, m);
+            nz += m > 0u ? 1u : 0u;
         }
     }
     const uint32_t msum = (uint32_t)wave_sum_i((int32_t)ms);
     const uint32_t mmax = (uint32_t)wave_max_i((int32_t)mx);
     const uint32_t ucap = (uint32_t)cap;
+    count = ucap;
     if (msum == 0)
         return 1u;  // no prefix token: any size
+    // A batch past the resident workgroups runs in rounds.  When its prefixes
+    // are (nearly) equal, whole sequences fill the rounds evenly and each
+    // extra round would start all its workgroups at once, unhidden: keep one
+    // range per sequence (it always fits: cap >= bs).
+    if (rounds) {
+        const uint32_t nonempty = (uint32_t)wave_sum_i((int32_t)nz);
+        if ((uint64_t)mmax * nonempty <= (uint64_t)msum + msum / 8u) {
+            count = nonempty;  // the workgroups of the other slots leave at once
+            return mmax;
+        }
+    }
     uint32_t lo = max((msum + ucap - 1u) / ucap, 1u);
-    if (batch_ranges(kv_indptr, qo_indptr, bs, lo, first) <= ucap)
+    const uint32_t nlo = batch_ranges(kv_indptr, qo_indptr, bs, lo, first);
+    if (nlo <= ucap) {
+        count = nlo;
         return lo;  // every uniform batch whose lengths are multiples of the size
+    }
     uint32_t hi = mmax;
     if (ucap > (uint32_t)bs)
         hi = min(hi, (msum + (ucap - (uint32_t)bs) - 1u) / (ucap - (uint32_t)bs));
     while (lo + 1u < hi) {  // count(lo) > cap >= count(hi)
         const uint32_t mid = lo + (hi - lo) / 2u;
-        if (batch_ranges(kv_indptr, qo_indptr, bs, mid, first) <= ucap)
+        const uint32_t n = batch_ranges(kv_indptr, qo_indptr, bs, mid, first);
+        if (n <= ucap) {
             hi = mid;
-        else
+            count = n;
+        } else {
             lo = mid;
+        }
     }
     return hi;
 }
 
-// Range size of modes 0 and 2 in units of 64 tokens.
+// Range size of modes 0, 2 and 3 in units of 64 tokens; `count` as for
+// fitted_range_units.
 template <int NC>
 __device__ __forceinline__ uint32_t range_units(const int32_t *kv_indptr, const int32_t *qo_indptr, int32_t bs,
                                                 int32_t mode, int32_t split_tokens, int32_t cap,
-                                                const SeqGroup<NC> &first)
+                                                const SeqGroup<NC> &first, uint32_t &count)
 {
-    return mode == 2 ? (uint32_t)split_tokens >> 6 : fitted_range_units<NC>(kv_indptr, qo_indptr, bs, cap, first);
+    if (mode == 2) {
+        count = (uint32_t)cap;
+        return (uint32_t)split_tokens >> 6;
+    }
+    return fitted_range_units<NC>(kv_indptr, qo_indptr, bs, cap, mode == 3, first, count);
 }
 
 // Mode 1: range `cidx` -> its sequence, token range and index pointers.
@@ -306,14 +337,17 @@ __device__ __forceinline__ int wave_scan_incl(int x)
     return x + (lane >= 16 ? t0 : 0) + (lane >= 32 ? t1 : 0) + (lane >= 48 ? t2 : 0);
 }
 
-// Modes 0 and 2: range `cidx` -> its sequence, token range and index
-// pointers, for ranges of 64 k tokens numbered sequence by sequence.
+// Modes 0, 2 and 3: range `cidx` -> its sequence, token range and index
+// pointers, for ranges of 64 k tokens numbered sequence by sequence (`count`:
+// a bound on the number of ranges; slots past it hold none).
 template <int NC>
 __device__ __forceinline__ Range locate_split_range(const int32_t *kv_indptr, const int32_t *qo_indptr,
-                                                    int32_t bs, uint32_t k, int64_t cidx,
+                                                    int32_t bs, uint32_t k, int64_t cidx, uint32_t count,
                                                     const SeqGroup<NC> &first)
 {
     Range r = {0, 0, 0, 0, 0, 0, false};
+    if (cidx >= (int64_t)count)
+        return r;
     const int32_t c_tok = (int32_t)(k << 6);
     int64_t cum = 0;
     for (int32_t b0 = 0; b0 < bs; b0 += 64 * NC) {
@@ -670,13 +704,15 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64, 2) void prefix_kernel(
     } else if (bs <= 64) {
         const SeqGroup<1> first = load_group<1>(kv_indptr, qo_indptr, bs, 0);
         early_copies();
-        const uint32_t k = range_units<1>(kv_indptr, qo_indptr, bs, mode, split_tokens, range_cap, first);
-        rg = locate_split_range<1>(kv_indptr, qo_indptr, bs, k, cidx, first);
+        uint32_t count;
+        const uint32_t k = range_units<1>(kv_indptr, qo_indptr, bs, mode, split_tokens, range_cap, first, count);
+        rg = locate_split_range<1>(kv_indptr, qo_indptr, bs, k, cidx, count, first);
     } else {
         const SeqGroup<8> first = load_group<8>(kv_indptr, qo_indptr, bs, 0);
         early_copies();
-        const uint32_t k = range_units<8>(kv_indptr, qo_indptr, bs, mode, split_tokens, range_cap, first);
-        rg = locate_split_range<8>(kv_indptr, qo_indptr, bs, k, cidx, first);
+        uint32_t count;
+        const uint32_t k = range_units<8>(kv_indptr, qo_indptr, bs, mode, split_tokens, range_cap, first, count);
+        rg = locate_split_range<8>(kv_indptr, qo_indptr, bs, k, cidx, count, first);
     }
     const int rows = p.rows;
     if (!rg.valid) {

@@ -149,7 +149,8 @@ int make_plan(const va_desc_t *d, int32_t l_ext, int32_t num_cus, va_plan_t *pla
         return fail(VA_ERR_SIZE, "rows per KV head (%lld) too large", (long long)rows);
     p.rows = (int32_t)rows;
     p.row_chunks = (int32_t)((rows + kRowChunk - 1) / kRowChunk);
-    p.tile_tokens = tile_tokens_for(d->head_dim, d->v_head_dim, d->kv_dtype == VA_DTYPE_FP8_E4M3FN ? 1 : 2);
+    const int kv_elem_bytes = d->kv_dtype == VA_DTYPE_FP8_E4M3FN ? 1 : 2;
+    p.tile_tokens = tile_tokens_for(d->head_dim, d->v_head_dim, kv_elem_bytes);
     const int64_t T = d->num_kv_indices;
     int64_t ranges;  // prefix workgroups per (KV head, row chunk)
     if (d->n_splits > 0) {
@@ -181,9 +182,21 @@ int make_plan(const va_desc_t *d, int32_t l_ext, int32_t num_cus, va_plan_t *pla
         int64_t c = (T * units + target - 1) / target;
         c = align_up(c < kSplitQuantum ? kSplitQuantum : c, kSplitQuantum);
         p.split_tokens = (int32_t)std::min<int64_t>(c, (int64_t)1 << 30);
-        ranges = T > 0 ? std::max<int64_t>(std::min<int64_t>(target / units, (T + kSplitQuantum - 1) / kSplitQuantum),
+        const int64_t resident = target / units;  // ranges per (KV head, row chunk) resident at once
+        ranges = T > 0 ? std::max<int64_t>(std::min<int64_t>(resident, (T + kSplitQuantum - 1) / kSplitQuantum),
                                            d->bs)
                        : 0;
+        if (d->bs > resident) {
+            // More sequences than resident workgroups: the grid runs in rounds,
+            // and with one range per sequence a ragged batch ends on a few long
+            // sequences.  Allow ranges of about kRoundRangeBytes of K/V per KV
+            // head, so that the dispatcher balances the rounds (mode 3: the
+            // kernels keep whole sequences when the prefixes are near equal).
+            p.mode = 3;
+            const int64_t tok_bytes = (int64_t)(d->head_dim + d->v_head_dim) * kv_elem_bytes;
+            const int64_t c_round = std::max<int64_t>(kSplitQuantum, kRoundRangeBytes / tok_bytes);
+            ranges = std::max<int64_t>(ranges, (T + c_round - 1) / c_round);
+        }
     }
     p.range_slots = ranges;
     const int64_t slots = p.range_slots * d->h_kv;

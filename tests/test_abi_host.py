@@ -128,10 +128,15 @@ def test_plan_headline_shapes():
     assert plan.workspace_bytes >= plan.range_slots * 2 * 32 * (256 * 2 + 4)
 
 
-def _fitted_units(lens, cap):
+def _fitted_units(lens, cap, rounds=False):
     """The kernels' mode-0 range size in units of 64 tokens, by plain search:
-    the smallest k >= 1 with sum_b ceil(ceil(n_b / 64) / k) <= cap."""
+    the smallest k >= 1 with sum_b ceil(ceil(n_b / 64) / k) <= cap.  In mode 3
+    (rounds=True) a batch whose longest prefix is within 1/8 of the mean over
+    its non-empty ones keeps whole sequences."""
     m = [-(-n // 64) for n in lens]
+    nz = sum(1 for x in m if x > 0)
+    if rounds and sum(m) > 0 and max(m) * nz <= sum(m) + sum(m) // 8:
+        return max(m)
     k = 1
     while sum(-(-x // k) for x in m) > cap:
         k += 1
@@ -148,8 +153,9 @@ def _meta_with_indices(bs, T, **kw):
 def test_ragged_batches_fit_the_resident_workgroups(seed):
     # Mode 0 (heuristic): the grid holds one range per resident prefix
     # workgroup (two 4-wave workgroups per CU here), at least one per sequence
-    # and at most ceil(T / 64); the kernels fit the range size to the lengths
-    # so that a ragged batch never needs more ranges than that.
+    # and at most ceil(T / 64) -- or, for a batch past the resident
+    # workgroups, about one per MiB of K/V; the kernels fit the range size to
+    # the lengths so that a ragged batch never needs more ranges than that.
     g = torch.Generator().manual_seed(seed)
     bs = int(torch.randint(1, 40, (1,), generator=g))
     lens = torch.randint(0, 5000, (bs,), generator=g).tolist()
@@ -157,7 +163,7 @@ def test_ragged_batches_fit_the_resident_workgroups(seed):
     meta = _meta_with_indices(bs, T, l_ext=2, h_q=8, h_kv=1, d=128)
     for cus in (8, 80, 256):
         plan = va.verify_attn_plan(va.make_desc(**meta), 2, cus)
-        assert plan.mode == 0
+        assert plan.mode == (3 if bs > 2 * cus else 0)
         c = plan.split_tokens
         assert c % 64 == 0 and c >= 64
         cap = plan.prefix_blocks  # one KV head, one row chunk
@@ -165,8 +171,11 @@ def test_ragged_batches_fit_the_resident_workgroups(seed):
         if T == 0:
             assert cap == 0
             continue
-        assert cap == max(min(2 * cus, -(-T // 64)), bs)
-        k = _fitted_units(lens, cap)
+        expect = max(min(2 * cus, -(-T // 64)), bs)
+        if bs > 2 * cus:  # rounds of workgroups: ~1 MiB of K/V (2048 tokens here) a range
+            expect = max(expect, -(-T // 2048))
+        assert cap == expect
+        k = _fitted_units(lens, cap, rounds=plan.mode == 3)
         assert sum(-(-n // (64 * k)) for n in lens) <= cap
         assert k * 64 <= -(-max(lens) // 64) * 64  # never longer than one range per sequence
 
@@ -202,15 +211,20 @@ def test_workspace_is_an_upper_bound_for_smaller_calls(shape, split):
     # max_bs for the same reason): the size never decreases as T or bs grow.
     max_bs, t_max = 24, 200_000
     l_ext = shape["l_ext"]
+    for cus in (256, 4):  # 4 CUs: batches past the resident workgroups, split for the rounds
+        _check_workspace_monotone(shape, split, max_bs, t_max, l_ext, cus)
+
+
+def _check_workspace_monotone(shape, split, max_bs, t_max, l_ext, cus):
     ts = sorted(set([0, 1, 63, 64, 65, 127, 129, 1000, 4095, 4097, 13423, 16423, 65536, t_max] +
                     list(range(0, t_max + 1, 997))))
     top = va.verify_attn_workspace_bytes(va.make_desc(**_meta_with_indices(max_bs, t_max, **shape), **split),
-                                         l_ext, 256)
+                                         l_ext, cus)
     for bs in (1, 2, 7, 8, 23, 24):
         prev = -1
         for T in ts:
             n = va.verify_attn_workspace_bytes(va.make_desc(**_meta_with_indices(bs, T, **shape), **split),
-                                               l_ext, 256)
+                                               l_ext, cus)
             assert n >= prev, (bs, T, n, prev)
             assert n <= top, (bs, T, n, top)
             prev = n
@@ -218,9 +232,32 @@ def test_workspace_is_an_upper_bound_for_smaller_calls(shape, split):
         prev = -1
         for bs in range(1, max_bs + 1):
             n = va.verify_attn_workspace_bytes(va.make_desc(**_meta_with_indices(bs, T, **shape), **split),
-                                               l_ext, 256)
+                                               l_ext, cus)
             assert n >= prev, (bs, T, n, prev)
             prev = n
+
+
+def test_batches_past_the_resident_workgroups_get_round_sized_ranges():
+    # 512 sequences, 16/2 heads, D=256 on 256 CUs: 256 ranges per KV head are
+    # resident, so the grid runs in rounds; ranges of ~1 MiB of K/V per KV
+    # head (1024 tokens) let a ragged batch balance instead of ending on its
+    # longest sequences.  A batch within the resident workgroups keeps one
+    # range per resident workgroup.
+    T = 512 * 2560
+    plan = va.verify_attn_plan(va.make_desc(**_meta_with_indices(512, T, l_ext=1, h_q=16, h_kv=2, d=256)), 1, 256)
+    assert plan.mode == 3 and plan.range_slots == -(-T // 1024)
+    # ragged: the kernels split the long sequences; near-equal: whole sequences
+    g = torch.Generator().manual_seed(3)
+    ragged = torch.randint(1024, 4097, (512,), generator=g).tolist()
+    assert _fitted_units(ragged, plan.range_slots, rounds=True) < -(-max(ragged) // 64)
+    equal = [2560] * 500 + [2400] * 12
+    assert _fitted_units(equal, plan.range_slots, rounds=True) == 40
+    plan = va.verify_attn_plan(va.make_desc(**_meta_with_indices(256, T, l_ext=1, h_q=16, h_kv=2, d=256)), 1, 256)
+    assert plan.mode == 0 and plan.range_slots == 256
+    # fp8, D = 128: 256 bytes a token -> 4096-token ranges
+    plan = va.verify_attn_plan(va.make_desc(**_meta_with_indices(
+        600, 600 * 3000, l_ext=1, h_q=8, h_kv=1, d=128, kv_dtype=torch.float8_e4m3fn)), 1, 256)
+    assert plan.range_slots == max(600, -(-600 * 3000 // 4096))
 
 
 def test_explicit_split_tokens_are_kept():

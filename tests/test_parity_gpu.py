@@ -145,6 +145,9 @@ def _hint_and_fit(va, p, num_kv_indices=None):
     plan = va.verify_attn_plan(va.make_desc(p.q, p.k_ext, p.v_ext, p.k_buf, p.v_buf, idx, out, p.bs),
                                p.l_ext)
     m = [-(-n // 64) for n in p.prefix_lens]
+    nz = sum(1 for x in m if x > 0)
+    if plan.mode == 3 and sum(m) > 0 and max(m) * nz <= sum(m) + sum(m) // 8:
+        return plan.split_tokens, 64 * max(m)  # near-equal prefixes in rounds: whole sequences
     k = 1
     while sum(-(-x // k) for x in m) > plan.range_slots:
         k += 1
@@ -187,6 +190,24 @@ def test_large_batches(va, bs, l_ext, hq, hkv, d, kv):
                        seed=bs + 1, name="bs %d" % bs)
     check_full(va, p)
     check_full(va, p, split_tokens=128)
+
+
+@pytest.mark.parametrize("spread", [0, 200, 1800])
+def test_batches_in_rounds_whole_or_split(va, spread):
+    # 520 sequences (16/2 heads, D = 256, decode) of up to 2048 tokens: more
+    # than the resident prefix workgroups, so the heuristic plans rounds and a
+    # grid of about one range per MiB of K/V per KV head.  Prefixes within 1/8
+    # of equal keep one range per sequence (the surplus slots hold none); a
+    # wider spread is cut into ranges.
+    g = torch.Generator().manual_seed(90 + spread)
+    lens = (2048 - torch.randint(0, spread + 1, (520,), generator=g)).tolist()
+    p = W.make_problem(lens, 1, 16, 2, 256, pool_factor=2, permute=True, seed=91, name="rounds")
+    hint, fit = _hint_and_fit(va, p)
+    if spread <= 200:
+        assert fit == -(-max(lens) // 64) * 64
+    else:
+        assert fit < -(-max(lens) // 64) * 64
+    check_full(va, p)
 
 
 def test_one_long_sequence_among_short_ones(va):
