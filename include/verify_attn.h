@@ -121,7 +121,7 @@ typedef struct {
     int32_t mode;            /* 0: heuristic (range size fitted on the device); 1: n_splits equal
                                 ranges per sequence; 2: ranges of split_tokens tokens; 3: the
                                 heuristic for a batch past the resident workgroups (rounds) */
-    int32_t split_tokens;    /* mode 2: tokens per range; mode 0: the size num_kv_indices tokens in
+    int32_t split_tokens;    /* mode 2: tokens per range; modes 0, 3: the size num_kv_indices tokens in
                                 equal prefixes would get (where the kernels guess each range starts) */
     int32_t n_splits;        /* ranges per sequence (mode 1) */
     int32_t rows;            /* query rows per KV head: (h_q / h_kv) * l_ext */

@@ -76,7 +76,7 @@ struct PrefixParams {
     int32_t page_size;
     uint16_t *part_o;  // [range_slots * h_kv, rows, D] bf16 (round to nearest even)
     float *part_lse;   // [range_slots * h_kv, rows]    fp32 (natural log)
-    int32_t *seq_ranges;  // [bs][2]: first range and range count of each sequence (modes 0, 2)
+    int32_t *seq_ranges;  // [bs][2]: first range and range count of each sequence (modes 0, 2, 3)
     int64_t q_s0, q_s1;        // elements
     uint32_t kb_s0, vb_s0;     // pool row strides, bytes (< 2^32, checked on the host)
     int64_t kb_s1, vb_s1;      // pool head strides, bytes
@@ -95,7 +95,7 @@ struct CombineParams {
     const int32_t *kv_indptr;
     const uint16_t *part_o;
     const float *part_lse;
-    const int32_t *seq_ranges;  // written by the prefix pass (modes 0, 2)
+    const int32_t *seq_ranges;  // written by the prefix pass (modes 0, 2, 3)
     uint16_t *out;
     const uint8_t *mask;          // tree mask bytes, or NULL for the causal draft block
     const int64_t *mask_indptr;   // [bs + 1] byte offsets of each sequence's mask

@@ -168,7 +168,7 @@ struct Range {
     int32_t end;
     int32_t kv_base;  // kv_indptr[b]
     int32_t qo;       // qo_indptr[b]
-    int32_t seq_ranges;  // ranges of sequence b (modes 0, 2)
+    int32_t seq_ranges;  // ranges of sequence b (modes 0, 2, 3)
     bool valid;
 };
 
@@ -663,9 +663,9 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64, 2) void prefix_kernel(
     };
 
     // ---- range ----
-    // Modes 0 and 2 cut every prefix into ranges of c tokens; split_tokens is
-    // c itself (mode 2) or the planner's estimate of it (mode 0: the size that
-    // num_kv_indices tokens in equal prefixes would get).  If every prefix is
+    // Modes 0, 2 and 3 cut every prefix into ranges of c tokens; split_tokens
+    // is c itself (mode 2) or the planner's estimate of it (modes 0 and 3: the
+    // size that num_kv_indices tokens in equal prefixes would get).  If every prefix is
     // a multiple of it, range cidx starts at kv_indices position
     // cidx * split_tokens: its first three index copies go out before the
     // index pointers are read, and are used if the range really starts there.
@@ -720,7 +720,7 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64, 2) void prefix_kernel(
         return;        // (never read by the combine pass)
     }
     // the first range of each sequence records where the sequence's ranges
-    // sit, for the combine pass (modes 0 and 2; mode 1 needs no table)
+    // sit, for the combine pass (modes 0, 2 and 3; mode 1 needs no table)
     if (mode != 1 && kvh == 0 && rc == 0 && rg.start == 0 && tid == 0)
         ((i32x2_t *)p.seq_ranges)[rg.b] = i32x2_t{(int32_t)cidx, rg.seq_ranges};
     const int64_t slot = cidx * h_kv + kvh;
@@ -1175,7 +1175,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
 
     // ---- first load round: where this sequence's rows and ranges are ----
     const int qo = qo_indptr[b];
-    // modes 0 and 2: the prefix pass recorded the sequence's first range and
+    // modes 0, 2 and 3: the prefix pass recorded the sequence's first range and
     // range count (only for sequences with a prefix; an empty one has none)
     const int32_t k0 = kv_indptr[b], k1 = kv_indptr[b + 1];
     const i32x2_t tab = ((const i32x2_t *)p.seq_ranges)[b];
