@@ -206,10 +206,27 @@ __device__ __forceinline__ uint32_t seq_len(const SeqGroup<NC> &g, int c, int32_
     return b0 + 64 * c + (int32_t)(threadIdx.x & 63) < bs ? (uint32_t)(g.k1[c] - g.k0[c]) : 0u;
 }
 
-// ranges of 64 k tokens that cover a prefix of n tokens
-__device__ __forceinline__ uint32_t ranges_for(uint32_t n, uint32_t k)
+// Division by a wave-uniform k >= 1.  With m = floor((2^32 - 1) / k), taken
+// once per k, x * m / 2^32 falls below x / k by x (1 + (2^32 - 1) mod k) /
+// (k 2^32) < 1 for every 32-bit x, so floor(x m / 2^32) is floor(x / k) or
+// one less, and one comparison of the remainder settles it: a multiply-high
+// and a correction per lane instead of a full division.
+struct UniformDiv {
+    uint32_t k, m;
+};
+
+__device__ __forceinline__ UniformDiv uniform_div(uint32_t k) { return UniformDiv{k, 0xffffffffu / k}; }
+
+__device__ __forceinline__ uint32_t div_floor(uint32_t x, const UniformDiv &d)
 {
-    return (((n + 63u) >> 6) + k - 1u) / k;
+    const uint32_t q = __umulhi(x, d.m);
+    return x - q * d.k >= d.k ? q + 1u : q;
+}
+
+// ranges of 64 k tokens that cover a prefix of n tokens
+__device__ __forceinline__ uint32_t ranges_for(uint32_t n, const UniformDiv &d)
+{
+    return div_floor(((n + 63u) >> 6) + d.k - 1u, d);
 }
 
 // number of ranges of 64 k tokens the whole batch needs (whole-wave call)
@@ -217,12 +234,13 @@ template <int NC>
 __device__ __forceinline__ uint32_t batch_ranges(const int32_t *kv_indptr, const int32_t *qo_indptr, int32_t bs,
                                                  uint32_t k, const SeqGroup<NC> &first)
 {
+    const UniformDiv d = uniform_div(k);
     uint32_t t = 0;
     for (int32_t b0 = 0; b0 < bs; b0 += 64 * NC) {
         const SeqGroup<NC> g = b0 == 0 ? first : load_group<NC>(kv_indptr, qo_indptr, bs, b0);
 #pragma unroll
         for (int c = 0; c < NC; ++c)
-            t += ranges_for(seq_len(g, c, b0, bs), k);
+            t += ranges_for(seq_len(g, c, b0, bs), d);
     }
     return (uint32_t)wave_sum_i((int32_t)t);
 }
@@ -251,7 +269,6 @@ __device__ __forceinline__ uint32_t fitted_range_units(const int32_t *kv_indptr,
         }
     }
     const uint32_t msum = (uint32_t)wave_sum_i((int32_t)ms);
-    const uint32_t mmax = (uint32_t)wave_max_i((int32_t)mx);
     const uint32_t ucap = (uint32_t)cap;
     count = ucap;
     if (msum == 0)
@@ -261,6 +278,7 @@ __device__ __forceinline__ uint32_t fitted_range_units(const int32_t *kv_indptr,
     // extra round would start all its workgroups at once, unhidden: keep one
     // range per sequence (it always fits: cap >= bs).
     if (rounds) {
+        const uint32_t mmax = (uint32_t)wave_max_i((int32_t)mx);
         const uint32_t nonempty = (uint32_t)wave_sum_i((int32_t)nz);
         if ((uint64_t)mmax * nonempty <= (uint64_t)msum + msum / 8u) {
             count = nonempty;  // the workgroups of the other slots leave at once
@@ -273,7 +291,7 @@ __device__ __forceinline__ uint32_t fitted_range_units(const int32_t *kv_indptr,
         count = nlo;
         return lo;  // every uniform batch whose lengths are multiples of the size
     }
-    uint32_t hi = mmax;
+    uint32_t hi = (uint32_t)wave_max_i((int32_t)mx);
     if (ucap > (uint32_t)bs)
         hi = min(hi, (msum + (ucap - (uint32_t)bs) - 1u) / (ucap - (uint32_t)bs));
     while (lo + 1u < hi) {  // count(lo) > cap >= count(hi)
@@ -348,6 +366,7 @@ __device__ __forceinline__ Range locate_split_range(const int32_t *kv_indptr, co
     Range r = {0, 0, 0, 0, 0, 0, false};
     if (cidx >= (int64_t)count)
         return r;
+    const UniformDiv d = uniform_div(k);
     const int32_t c_tok = (int32_t)(k << 6);
     int64_t cum = 0;
     for (int32_t b0 = 0; b0 < bs; b0 += 64 * NC) {
@@ -355,7 +374,7 @@ __device__ __forceinline__ Range locate_split_range(const int32_t *kv_indptr, co
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             const uint32_t n = seq_len(g, c, b0, bs);
-            const int32_t nch = (int32_t)ranges_for(n, k);
+            const int32_t nch = (int32_t)ranges_for(n, d);
             const int32_t incl = wave_scan_incl(nch);
             const int32_t total = lane_i(incl, 63);
             if (cidx < cum + total) {
