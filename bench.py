@@ -173,6 +173,7 @@ def time_workload(torch, va, W, name, steps, warmup, replicas, seed0=1000, capac
     torch.cuda.synchronize()
     pre = [ev[i][0].elapsed_time(ev[i][1]) for i in range(steps)]
     com = [ev[i][1].elapsed_time(ev[i][2]) for i in range(steps)]
+    call = sorted(ev[i][0].elapsed_time(ev[i][2]) for i in range(steps))
 
     # ---- warm cache: one replica over and over ----
     def warm_step(i):
@@ -245,6 +246,8 @@ def time_workload(torch, va, W, name, steps, warmup, replicas, seed0=1000, capac
         prefix_us_mean=us(pre_ms), prefix_us_median=us(statistics.median(pre)),
         prefix_us_p10=us(sorted(pre)[len(pre) // 10]), prefix_us_p90=us(sorted(pre)[(9 * len(pre)) // 10]),
         combine_us_mean=us(statistics.mean(com)),
+        call_us_median=us(statistics.median(call)), call_us_p10=us(call[len(call) // 10]),
+        call_us_p90=us(call[(9 * len(call)) // 10]),
         prefix_gbs=kv_bytes / (pre_ms * 1e-3) / 1e9,
         prefix_us_b2b=us(ms_prefix_b2b), prefix_gbs_b2b=kv_bytes / (ms_prefix_b2b * 1e-3) / 1e9,
         us_step_warm=us(ms_warm), gbs_warm=kv_bytes / (ms_warm * 1e-3) / 1e9,
@@ -532,6 +535,9 @@ def main():
             "prefix_us_per_launch_events": {"mean": head["prefix_us_mean"], "median": head["prefix_us_median"],
                                             "p10": head["prefix_us_p10"], "p90": head["prefix_us_p90"]},
             "combine_us_mean": head["combine_us_mean"],
+            # one event pair around each whole call (both passes), cold
+            "call_us_per_call_events": {"median": head["call_us_median"], "p10": head["call_us_p10"],
+                                        "p90": head["call_us_p90"]},
             "warm_cache": {"us_per_call": head["us_step_warm"], "gbs": round(head["gbs_warm"], 2)},
             "graph_replay": {"us_per_call": head["us_step_graph"],
                              "gbs": round(head["gbs_graph"], 2) if head["gbs_graph"] else None,

@@ -366,21 +366,23 @@ class VerifyAttn:
     reason).  The library's workspace size never decreases as the batch or
     the index count grow, so every call with ``bs <= max_bs`` and
     ``len(kv_indices) <= max_kv_indices`` fits; ``kv_indices`` may be a buffer
-    of fixed capacity whose used part ``kv_indptr`` delimits.
+    of fixed capacity whose used part ``kv_indptr`` delimits.  ``v_head_dim``
+    (default ``head_dim``) is the value head dim the partials are sized by.
     """
 
     def __init__(self, h_q, h_kv, head_dim, l_ext, kv_dtype, max_bs, max_kv_indices, device,
-                 split_tokens=0, n_splits=0):
+                 split_tokens=0, n_splits=0, v_head_dim=None):
         self.l_ext = int(l_ext)
         self.device = torch.device(device)
         self.split_tokens, self.n_splits = int(split_tokens), int(n_splits)
+        dv = int(head_dim if v_head_dim is None else v_head_dim)
         dummy = lambda *s: torch.empty(*s, dtype=torch.bfloat16, device="meta")
         d = make_desc(dummy(max_bs * l_ext, h_q, head_dim), dummy(max_bs * l_ext, h_kv, head_dim),
-                      dummy(max_bs * l_ext, h_kv, head_dim),
+                      dummy(max_bs * l_ext, h_kv, dv),
                       torch.empty(1, h_kv, head_dim, dtype=kv_dtype, device="meta"),
-                      torch.empty(1, h_kv, head_dim, dtype=kv_dtype, device="meta"),
+                      torch.empty(1, h_kv, dv, dtype=kv_dtype, device="meta"),
                       torch.empty(max_kv_indices, dtype=torch.int64, device="meta"),
-                      dummy(max_bs * l_ext, h_q, head_dim), max_bs, split_tokens, n_splits)
+                      dummy(max_bs * l_ext, h_q, dv), max_bs, split_tokens, n_splits)
         with torch.cuda.device(self.device):
             self.workspace = alloc_workspace(d, l_ext, self.device)
 

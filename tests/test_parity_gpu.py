@@ -274,6 +274,24 @@ def test_value_head_dim_differs_long_and_split(va):
     check_full(va, p, n_splits=16)
 
 
+def test_fixed_runner_with_value_head_dim_and_smaller_calls(va):
+    # VerifyAttn sized once (6 sequences, 15000 indices, D = 128 / Dv = 256:
+    # the partials it holds are sized by Dv) serves calls with fewer
+    # sequences and fewer indices from the same workspace
+    runner = va.VerifyAttn(8, 2, 128, 4, torch.bfloat16, max_bs=6, max_kv_indices=15000, device=dev(),
+                           v_head_dim=256)
+    ws = runner.workspace.data_ptr()
+    for lens, seed in (([1000, 2000, 2000], 70), ([5000], 71), ([64, 0, 3000, 10, 700, 1200], 72)):
+        p = W.make_problem(lens, 4, 8, 2, 128, 256, k_scale=0.5, v_scale=0.25, pool_factor=2, permute=True,
+                           seed=seed, name="fixed runner, %d sequences" % len(lens))
+        pg = p.to(dev())
+        out = runner(pg.q, pg.k_ext, pg.v_ext, pg.k_buf, pg.v_buf, pg.qo_indptr, pg.kv_indptr, pg.kv_indices,
+                     pg.sm_scale, k_scale=pg.k_scale, v_scale=pg.v_scale)
+        torch.cuda.synchronize()
+        assert runner.workspace.data_ptr() == ws
+        assert_close(out, oracle_of(p), BF16_TOL, p.name)
+
+
 def test_many_rows_two_row_chunks(va):
     # G=16, l_ext=8: 128 query rows per KV head -> two 64-row chunks
     check_full(va, W.make_problem([700, 1500], 8, 16, 1, 128, seed=57, name="128 rows"))
