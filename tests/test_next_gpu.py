@@ -257,13 +257,20 @@ def test_paged_headline_shape(va):
 
 
 # ---------------------------------------------- decode and draft-extend reuse ---
-@pytest.mark.parametrize("name", ["decode_b64", "draft_extend_b16"])
+@pytest.mark.parametrize("name", ["decode_b64", "draft_extend_b16", "decode_b512"])
 def test_reuse_modes_sampled(va, name):
+    # decode_b512 runs past the resident prefix workgroups (ranges of about
+    # 1 MiB of K/V per KV head, in rounds): its sample adds the first, the
+    # last and the longest sequences to 21 random ones
     p = W.CONFIGS[name]()
     pg = p.to(dev())
     out = run_gpu(va, pg)
     gen = torch.Generator().manual_seed(5)
-    bsel = torch.randperm(p.bs, generator=gen)[:6].tolist()
+    if p.bs > 64:
+        longest = max(range(p.bs), key=lambda b: p.prefix_lens[b])
+        bsel = sorted(set(torch.randperm(p.bs, generator=gen)[:21].tolist() + [0, p.bs - 1, longest]))
+    else:
+        bsel = torch.randperm(p.bs, generator=gen)[:6].tolist()
     sel = [(b, h) for b in bsel for h in (0, 7, 15)]
     ref = oracle.verify_attn(p.q, p.k_ext, p.v_ext, p.k_buf, p.v_buf, p.qo_indptr, p.kv_indptr,
                              p.kv_indices, p.sm_scale, p.k_scale, p.v_scale, select=sel)
