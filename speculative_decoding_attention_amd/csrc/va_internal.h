@@ -35,6 +35,13 @@ constexpr int kSplitQuantum = 64;
 // of about this many K/V bytes per KV head let the dispatcher balance the
 // rounds of workgroups (1024 tokens at bf16 D = Dv = 256).
 constexpr int64_t kRoundRangeBytes = int64_t(1) << 20;
+// Those ranges in tokens (a multiple of kSplitQuantum, at least one): the
+// planner sizes the grid with it and the kernels bound their fit with it.
+constexpr int round_range_tokens(int head_dim, int v_head_dim, int elem_bytes)
+{
+    const int64_t c = kRoundRangeBytes / ((int64_t)(head_dim + v_head_dim) * elem_bytes) / kSplitQuantum * kSplitQuantum;
+    return c >= kSplitQuantum ? (int)c : kSplitQuantum;
+}
 // Size of the library-owned device array verify_attn_run_noalloc keeps its
 // partials in (va_noalloc.hip): the headline and 64k-prefix workloads need
 // 8.5 MB of it on MI355X.

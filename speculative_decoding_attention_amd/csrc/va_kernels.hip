@@ -251,28 +251,39 @@ __device__ __forceinline__ uint32_t batch_ranges(const int32_t *kv_indptr, const
 // [ceil(M / cap), ceil(M / (cap - bs))] (when cap > bs) and never above
 // max m_b; a binary search over whole-batch counts takes it from there.
 // `count` receives the number of ranges when it is known on the way (else
-// cap, an upper bound).
+// cap, an upper bound).  In rounds (mode 3, a batch past the resident
+// workgroups) the planner's grid holds max(bs, ceil(T / round_tokens))
+// ranges for the T of num_kv_indices; the fit takes that bound for the T the
+// batch really has, so a kv_indices buffer of larger capacity splits the
+// batch exactly as one of its own length, and a workgroup whose slot `cidx`
+// lies past the bound leaves before the search.
 template <int NC>
 __device__ __forceinline__ uint32_t fitted_range_units(const int32_t *kv_indptr, const int32_t *qo_indptr,
-                                                       int32_t bs, int32_t cap, bool rounds,
-                                                       const SeqGroup<NC> &first, uint32_t &count)
+                                                       int32_t bs, int32_t cap, bool rounds, uint32_t round_tokens,
+                                                       int64_t cidx, const SeqGroup<NC> &first, uint32_t &count)
 {
-    uint32_t ms = 0, mx = 0, nz = 0;
+    uint32_t ms = 0, mx = 0, nz = 0, ns = 0;
     for (int32_t b0 = 0; b0 < bs; b0 += 64 * NC) {
         const SeqGroup<NC> g = b0 == 0 ? first : load_group<NC>(kv_indptr, qo_indptr, bs, b0);
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-            const uint32_t m = (seq_len(g, c, b0, bs) + 63u) >> 6;
+            const uint32_t n = seq_len(g, c, b0, bs);
+            const uint32_t m = (n + 63u) >> 6;
             ms += m;
             mx = max(mx, m);
             nz += m > 0u ? 1u : 0u;
+            ns += n;
         }
     }
     const uint32_t msum = (uint32_t)wave_sum_i((int32_t)ms);
-    const uint32_t ucap = (uint32_t)cap;
+    uint32_t ucap = (uint32_t)cap;
+    if (rounds) {
+        const uint32_t tokens = (uint32_t)wave_sum_i((int32_t)ns);
+        ucap = min(ucap, max((uint32_t)bs, (tokens + round_tokens - 1u) / round_tokens));
+    }
     count = ucap;
-    if (msum == 0)
-        return 1u;  // no prefix token: any size
+    if (msum == 0 || cidx >= (int64_t)ucap)
+        return 1u;  // no prefix token, or no range for this slot: any size
     // A batch past the resident workgroups runs in rounds.  When its prefixes
     // are (nearly) equal, whole sequences fill the rounds evenly and each
     // extra round would start all its workgroups at once, unhidden: keep one
@@ -312,13 +323,14 @@ __device__ __forceinline__ uint32_t fitted_range_units(const int32_t *kv_indptr,
 template <int NC>
 __device__ __forceinline__ uint32_t range_units(const int32_t *kv_indptr, const int32_t *qo_indptr, int32_t bs,
                                                 int32_t mode, int32_t split_tokens, int32_t cap,
-                                                const SeqGroup<NC> &first, uint32_t &count)
+                                                uint32_t round_tokens, int64_t cidx, const SeqGroup<NC> &first,
+                                                uint32_t &count)
 {
     if (mode == 2) {
         count = (uint32_t)cap;
         return (uint32_t)split_tokens >> 6;
     }
-    return fitted_range_units<NC>(kv_indptr, qo_indptr, bs, cap, mode == 3, first, count);
+    return fitted_range_units<NC>(kv_indptr, qo_indptr, bs, cap, mode == 3, round_tokens, cidx, first, count);
 }
 
 // Mode 1: range `cidx` -> its sequence, token range and index pointers.
@@ -716,6 +728,7 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64, 2) void prefix_kernel(
                      : "memory");
     };
     const int32_t range_cap = (int32_t)(gridDim.x / (uint32_t)(h_kv * row_chunks));  // ranges per (KV head, chunk)
+    constexpr uint32_t kRoundTokens = (uint32_t)round_range_tokens(D, DV, FP8 ? 1 : 2);
     Range rg;
     if (mode == 1) {
         early_copies();
@@ -724,13 +737,15 @@ __global__ __launch_bounds__(prefix_waves(NQB) * 64, 2) void prefix_kernel(
         const SeqGroup<1> first = load_group<1>(kv_indptr, qo_indptr, bs, 0);
         early_copies();
         uint32_t count;
-        const uint32_t k = range_units<1>(kv_indptr, qo_indptr, bs, mode, split_tokens, range_cap, first, count);
+        const uint32_t k = range_units<1>(kv_indptr, qo_indptr, bs, mode, split_tokens, range_cap, kRoundTokens,
+                                          cidx, first, count);
         rg = locate_split_range<1>(kv_indptr, qo_indptr, bs, k, cidx, count, first);
     } else {
         const SeqGroup<8> first = load_group<8>(kv_indptr, qo_indptr, bs, 0);
         early_copies();
         uint32_t count;
-        const uint32_t k = range_units<8>(kv_indptr, qo_indptr, bs, mode, split_tokens, range_cap, first, count);
+        const uint32_t k = range_units<8>(kv_indptr, qo_indptr, bs, mode, split_tokens, range_cap, kRoundTokens,
+                                          cidx, first, count);
         rg = locate_split_range<8>(kv_indptr, qo_indptr, bs, k, cidx, count, first);
     }
     const int rows = p.rows;

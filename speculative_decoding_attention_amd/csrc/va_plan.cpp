@@ -193,8 +193,7 @@ int make_plan(const va_desc_t *d, int32_t l_ext, int32_t num_cus, va_plan_t *pla
             // head, so that the dispatcher balances the rounds (mode 3: the
             // kernels keep whole sequences when the prefixes are near equal).
             p.mode = 3;
-            const int64_t tok_bytes = (int64_t)(d->head_dim + d->v_head_dim) * kv_elem_bytes;
-            const int64_t c_round = std::max<int64_t>(kSplitQuantum, kRoundRangeBytes / tok_bytes);
+            const int64_t c_round = round_range_tokens(d->head_dim, d->v_head_dim, kv_elem_bytes);
             ranges = std::max<int64_t>(ranges, (T + c_round - 1) / c_round);
         }
     }

@@ -210,6 +210,45 @@ def test_batches_in_rounds_whole_or_split(va, spread):
     check_full(va, p)
 
 
+@pytest.mark.parametrize("case", ["600 decode bf16", "600 decode fp8", "8 x 8192"])
+def test_capacity_buffer_splits_like_an_exact_one(va, case):
+    # kv_indices at 4x the batch's tokens (a graph-capture buffer) plans a
+    # larger grid, but the kernels fit the ranges to the tokens kv_indptr
+    # holds, so the split and every rounding match the exact buffer's: the
+    # outputs are bit-equal.  The 600-sequence batches run past the resident
+    # workgroups (plan mode 3, round-sized ranges); 8 x 8192 is mode 0.
+    g = torch.Generator().manual_seed(95)
+    if case == "8 x 8192":
+        p = W.make_problem([8192] * 8, 4, 16, 2, 256, k_scale=0.5, v_scale=0.25, pool_factor=2, permute=True,
+                           seed=96, name=case)
+    else:
+        lens = torch.randint(256, 2049, (600,), generator=g).tolist()
+        kv = torch.float8_e4m3fn if "fp8" in case else torch.bfloat16
+        hq, hkv, d = (16, 2, 256) if kv == torch.bfloat16 else (8, 1, 128)
+        p = W.make_problem(lens, 1, hq, hkv, d, kv_dtype=kv, pool_factor=2, permute=True, seed=97, name=case)
+    pg = p.to(dev())
+    cap = torch.zeros(4 * p.total_prefix, dtype=torch.int64, device=dev())
+    cap[:p.total_prefix].copy_(pg.kv_indices)
+    out_cap = torch.empty(pg.q.shape[0], p.h_q, p.v_head_dim, dtype=torch.bfloat16, device=dev())
+    plans = [va.verify_attn_plan(va.make_desc(pg.q, pg.k_ext, pg.v_ext, pg.k_buf, pg.v_buf, idx, out_cap, p.bs),
+                                 p.l_ext) for idx in (pg.kv_indices, cap)]
+    assert plans[0].mode == (0 if case == "8 x 8192" else 3)
+    if plans[0].mode == 3:
+        assert plans[1].prefix_blocks > plans[0].prefix_blocks
+    else:  # mode 0 sizes its grid by the resident workgroups alone
+        assert plans[1].prefix_blocks == plans[0].prefix_blocks
+    exact = run_gpu(va, pg)
+    va.verify_attn_run(pg.q, pg.k_ext, pg.v_ext, pg.k_buf, pg.v_buf, pg.qo_indptr, pg.kv_indptr, cap, p.l_ext,
+                       p.sm_scale, p.k_scale, p.v_scale, out=out_cap)
+    torch.cuda.synchronize()
+    assert torch.equal(exact, out_cap), "a capacity-sized kv_indices changed the split"
+    sel = [(b, h) for b in (0, p.bs // 2, p.bs - 1) for h in (0, p.h_q - 1)]
+    rows = np.zeros(out_cap.shape, dtype=bool)
+    for b, h in sel:
+        rows[b * p.l_ext:(b + 1) * p.l_ext, h] = True
+    assert_close(out_cap, oracle_of(p, select=sel), tol_of(p), case, mask=rows)
+
+
 def test_one_long_sequence_among_short_ones(va):
     # 40 sequences whose grid averages under 8 ranges each, so the combine
     # pass preloads 8 partial rows at a time; the 20000-token sequence has
