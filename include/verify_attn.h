@@ -87,8 +87,9 @@ typedef enum {
  * about one range per MiB of K/V per KV head -- and the kernels pick the
  * range size from kv_indptr on every launch: the smallest multiple of 64
  * tokens whose ranges fit that grid, or whole sequences for a batch past
- * the resident workgroups whose prefixes are within 1/8 of equal; so the
- * split follows the lengths actually passed):
+ * the resident workgroups whose prefixes are within 1/8 of equal, with the
+ * MiB-range bound taken for the tokens kv_indptr holds; so the split follows
+ * the lengths actually passed, whatever the capacity of kv_indices):
  *   split_tokens > 0 : every prefix is cut into ranges of split_tokens tokens
  *                      (a multiple of 64), one work item each;
  *   n_splits > 0     : the pages' rule -- every prefix is cut into n_splits
