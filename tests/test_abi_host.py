@@ -352,3 +352,64 @@ def test_paged_entry_rejects_bad_arguments():
     assert call(fake, 8, 0) == -13
     assert call(fake, -1, 16) == -7
     assert call(None, 8, 16) == -1
+
+
+C_CLIENT = r"""
+#include <stdio.h>
+#include <string.h>
+#include "verify_attn.h"
+
+/* 8 sequences of 8192 tokens, l_ext 4, 16/2 heads, D = Dv = 256, bf16 pool */
+int main(void)
+{
+    va_desc_t d;
+    va_plan_t p;
+    size_t ws = 0;
+    int rc;
+    memset(&d, 0, sizeof d);
+    d.bs = 8; d.h_q = 16; d.h_kv = 2; d.head_dim = 256; d.v_head_dim = 256;
+    d.kv_dtype = VA_DTYPE_BF16; d.q_rows = 32; d.num_kv_indices = 65536;
+    d.q_stride[0] = 16 * 256; d.q_stride[1] = 256;
+    d.out_stride[0] = 16 * 256; d.out_stride[1] = 256;
+    d.kext_stride[0] = d.vext_stride[0] = d.kbuf_stride[0] = d.vbuf_stride[0] = 2 * 256;
+    d.kext_stride[1] = d.vext_stride[1] = d.kbuf_stride[1] = d.vbuf_stride[1] = 256;
+    rc = verify_attn_plan(&d, 4, 256, &p);
+    if (rc == VA_OK)
+        rc = verify_attn_workspace_bytes(&d, 4, 256, &ws);
+    printf("%d %d %d %lld %lld %zu %zu %d\n", rc, p.mode, p.split_tokens, (long long)p.range_slots,
+           (long long)p.prefix_blocks, p.workspace_bytes, ws, verify_attn_version());
+    d.h_q = 15;  /* not a multiple of h_kv: rejected with a status, nothing launched */
+    rc = verify_attn_check(&d, 4);
+    printf("%d %s\n", rc, verify_attn_strerror(rc));
+    return 0;
+}
+"""
+
+
+def test_header_is_plain_c_and_links():
+    # The boundary is a C ABI: the header compiles as strict C99 and a C
+    # program links against the library and plans the headline shape
+    # without Python (no device needed for planning).
+    import shutil
+    import subprocess
+    import tempfile
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    pkg = os.path.dirname(va.LIB_PATH)
+    with tempfile.TemporaryDirectory() as tmp:
+        src, exe = os.path.join(tmp, "client.c"), os.path.join(tmp, "client")
+        with open(src, "w") as f:
+            f.write(C_CLIENT)
+        include = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+        subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I", include, src,
+                        "-o", exe, "-L", pkg, "-lverify_attn", "-Wl,-rpath," + pkg], check=True)
+        out = subprocess.run([exe], check=True, capture_output=True, text=True).stdout.split("\n")
+    rc, mode, split, slots, blocks, ws_plan, ws, version = (int(x) for x in out[0].split())
+    plan = va.verify_attn_plan(va.make_desc(**meta_problem(bs=8, n=8192)), 4, 256)
+    assert rc == 0 and version == va.lib().verify_attn_version()
+    assert (mode, split, slots, blocks, ws_plan) == (plan.mode, plan.split_tokens, plan.range_slots,
+                                                      plan.prefix_blocks, plan.workspace_bytes)
+    assert ws == ws_plan
+    code, msg = out[1].split(" ", 1)
+    assert int(code) == -3 and msg.strip()  # VA_ERR_HEADS
