@@ -496,6 +496,13 @@ GRAPH_CASES = {
         ("short", [64 * (i % 5) + 3 for i in range(16)]),
         ("two empty", [0, 9000] + [2000] * 13 + [0]),
     ]),
+    # decode batch past the resident prefix workgroups (plan mode 3): ragged
+    # lengths cut into round-sized ranges, near-equal ones kept whole
+    "bf16 decode 600": (600, 1, 16, 2, 256, torch.bfloat16, [
+        ("ragged", [256 + (i * 379) % 1793 for i in range(600)]),
+        ("near-equal", [1500 - (i % 7) * 10 for i in range(600)]),
+        ("some empty", [0 if i % 9 == 0 else 700 + (i * 131) % 900 for i in range(600)]),
+    ]),
 }
 
 
